@@ -1,0 +1,75 @@
+"""An independent second formulation, for pinning the oracle.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Instead of walking the table slot by slot, this version first turns a
+token's active slots into a multiset of pool rows: k_r = how many active
+slots name row r of a given pool.  Each distinct row then contributes
+k_r * e^{s_r} to the normaliser and k_r * e^{s_r} * row_r to the numerator,
+with no max-subtraction, evaluated in mpmath at 50 significant digits
+(mpmath's exponent range does not overflow).  Dot products of decoded inputs
+are computed exactly: every product of two BF16/E4M3 values is exact in
+binary64, and math.fsum returns the correctly rounded sum.
+
+It is slow, pure-Python, and only meant for tiny inputs (a handful of
+tokens and heads, pools of a few dozen rows).
+"""
+
+from __future__ import annotations
+
+import math
+from collections import Counter
+
+import mpmath
+import numpy as np
+
+from .formats import decode_bits
+
+_SWA = 128
+
+
+def brute_force_decode(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                       indices, topk_lens, sinks, bmm1_scale, bmm2_scale,
+                       lse_scale, dps: int = 50):
+    """Returns (out [T,H,D] float64, lse [T,H] float64)."""
+    b1 = mpmath.mpf(float(np.float32(bmm1_scale)))
+    b2 = mpmath.mpf(float(np.float32(bmm2_scale)))
+    g = mpmath.mpf(float(np.float32(lse_scale)))
+    T, H, D = q_bits.shape
+    K = indices.shape[1]
+    q = decode_bits(q_bits, q_dtype)
+    out = np.zeros((T, H, D))
+    lse = np.zeros((T, H))
+    with mpmath.workdps(dps):
+        for t in range(T):
+            n = K if topk_lens is None else int(topk_lens[t])
+            mult = Counter()
+            for c in range(K):
+                if c >= n:
+                    break
+                r = int(indices[t][c])
+                if r != -1:
+                    mult[(0 if c < _SWA else 1, r)] += 1
+            rows = {}
+            for (pool, r) in mult:
+                src = swa_bits if pool == 0 else comp_bits
+                rows[(pool, r)] = [float(v) for v in decode_bits(src[r], kv_dtype)]
+            for h in range(H):
+                qh = [float(v) for v in q[t, h]]
+                z = mpmath.mpf(0)
+                num = [mpmath.mpf(0)] * D
+                for key, k in mult.items():
+                    row = rows[key]
+                    dot = math.fsum(a * b for a, b in zip(qh, row))
+                    wgt = k * mpmath.exp(b1 * mpmath.mpf(dot))
+                    z += wgt
+                    num = [acc + wgt * mpmath.mpf(v) for acc, v in zip(num, row)]
+                if sinks is not None:
+                    z += mpmath.exp(mpmath.mpf(float(np.float32(sinks[h]))))
+                if z == 0:
+                    out[t, h] = 0.0
+                    lse[t, h] = -math.inf
+                    continue
+                out[t, h] = [float(b2 * v / z) for v in num]
+                lse[t, h] = float(g * mpmath.log(z, 2))
+    return out, lse
