@@ -1,0 +1,211 @@
+/*
+ * libsparsemla - sparse MLA decode with an index-driven KV gather, for
+ * AMD Instinct MI355X (gfx950).  C ABI: plain pointers, sizes and HIP
+ * streams; no C++ or framework types cross this boundary.
+ *
+ * The operation (FlashInfer "trtllm_batch_decode_sparse_mla_dsv4",
+ * introduction and parameters): every query token t carries H heads of 512
+ * dims (448 NoPE then 64 RoPE, per the "q" parameter of FlashInfer
+ * "cake_sparse_mla_sm120_dsv4_nvfp4_decode").  It attends only to the KV
+ * rows named by row t of an int32 table: columns 0..127 index the SWA pool,
+ * the other columns index the compressed pool, -1 masks a slot, and
+ * topk_lens[t] (which counts the 128 SWA columns) truncates the row.  Each
+ * KV row is one 512-d latent vector shared by every head as both key and
+ * value.  For head h, with s_c = bmm1_scale * <q[t,h,:], row_c> over the
+ * active slots c:
+ *
+ *   Z          = sum_c e^{s_c} + e^{sinks[h]}          (sink term if given)
+ *   out[t,h,:] = bf16( bmm2_scale * sum_c e^{s_c} row_c / Z )
+ *   out_lse    = lse_scale * log2(Z)
+ *
+ * Readings where the pages are silent: log2(e) is applied inside the
+ * library (bmm1_scale is the plain softmax scale times any FP8 scales, as
+ * the vLLM DeepseekV4FlashInferMLAAttention listing builds it); the sink is
+ * a natural-log logit that bmm1_scale does not multiply; out_lse includes
+ * the sink term; a token with no active slot gets out = 0 and
+ * out_lse = -inf (or lse_scale * sink * log2(e) with a sink); seq_lens and
+ * cum_seq_lens_q do not change the result (the table is authoritative).
+ *
+ * Conventions for every entry point:
+ *  - Ownership: the caller owns every buffer.  The library keeps no
+ *    per-call state, allocates no device memory and never synchronises
+ *    (except sparse_mla_get_device_error, which says so).
+ *  - Errors: each call returns an int status, SMLA_OK (0) on success.
+ *    Argument checks happen on the host before anything is launched; a
+ *    rejected call launches nothing.  Nothing is ever copied to fix a
+ *    layout: a wrong layout is an error (FlashInfer
+ *    "msa_sparse_decode_attention", parameter "out").
+ *  - Device pointers must point to memory of the device that is current
+ *    on the calling thread, and "stream" must belong to that device.
+ */
+#ifndef SPARSEMLA_H_
+#define SPARSEMLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t without including HIP headers; pass a hipStream_t (or 0 for
+ * the null stream). */
+typedef struct ihipStream_t* smla_stream_t;
+
+/* ---- status codes --------------------------------------------------- */
+#define SMLA_OK                      0
+#define SMLA_ERR_INVALID_ARG         1  /* null pointer, bad size or stride */
+#define SMLA_ERR_UNSUPPORTED_DTYPE   2  /* dtype pair not BF16/BF16, FP8/FP8, BF16/FP8 */
+#define SMLA_ERR_UNSUPPORTED_SHAPE   3  /* H not 64 or 128 */
+#define SMLA_ERR_WORKSPACE_TOO_SMALL 4
+#define SMLA_ERR_MISALIGNED          5  /* see the alignment rules below */
+#define SMLA_ERR_BAD_PLAN            6  /* plan fields inconsistent with the call */
+#define SMLA_ERR_HIP                 7  /* a HIP runtime call or launch failed */
+
+/* ---- element types -------------------------------------------------- */
+#define SMLA_DTYPE_BF16       0   /* bfloat16 */
+#define SMLA_DTYPE_FP8_E4M3FN 1   /* OCP FP8 E4M3FN, per-tensor scaled */
+
+/* ---- flags ---------------------------------------------------------- */
+/* Check every active index on the device and record the first violation
+ * (an index outside [0, rows) of its pool other than -1, or a topk_len
+ * outside [0, K]) in the workspace's error block; read it back with
+ * sparse_mla_get_device_error.  Violating slots are skipped either way:
+ * an out-of-range index is never dereferenced, with or without the flag. */
+#define SMLA_FLAG_VALIDATE_INDICES 1u
+
+/* Device-side error codes reported by sparse_mla_get_device_error. */
+#define SMLA_DEVERR_NONE          0
+#define SMLA_DEVERR_INDEX_RANGE   1
+#define SMLA_DEVERR_TOPK_LEN      2
+
+#define SMLA_HEAD_DIM     512
+#define SMLA_SWA_COLUMNS  128
+#define SMLA_MAX_SPLITS   64   /* hard cap of any plan (the planner's default cap is 16) */
+
+/* Split-K plan (FlashInfer "cake_sparse_mla_sm120_dsv4_nvfp4_decode":
+ * the resolved plan {head_tiles, num_splits, chunks_per_block}).  Table
+ * columns are cut into chunks of chunk_cols; split s covers columns
+ * [s*chunks_per_split*chunk_cols, (s+1)*chunks_per_split*chunk_cols).  A
+ * split whose columns are all inactive yields an empty partial. */
+typedef struct smla_plan {
+  int32_t num_splits;        /* S >= 1; S == 1 writes out/out_lse directly */
+  int32_t head_tiles;        /* always 1: one workgroup covers all heads */
+  int32_t chunk_cols;        /* columns per chunk */
+  int32_t chunks_per_split;  /* consecutive chunks per split */
+  int32_t num_chunks;        /* ceil(K / chunk_cols) */
+  int32_t K;                 /* table width the plan was made for */
+  int32_t reserved[2];
+} smla_plan;
+
+/* Arguments of sparse_mla_decode.  Field names follow the pages' statement
+ * of the problem (FlashInfer trtllm_batch_decode_sparse_mla_dsv4
+ * parameters).  All pointers are device pointers unless noted. */
+typedef struct smla_decode_args {
+  int32_t T;                   /* query tokens (flattened over requests); 0 = no-op */
+  int32_t H;                   /* heads per token: 64 or 128 (callers zero-pad,
+                                  vLLM get_padded_num_q_heads) */
+  int32_t K;                   /* table width (columns) >= 1 */
+  int32_t q_dtype;             /* SMLA_DTYPE_BF16 or SMLA_DTYPE_FP8_E4M3FN */
+  const void* q;               /* [T, H, 512] contiguous, 16-B aligned */
+  const void* swa_pool;        /* [swa_rows, row_stride] rows of 512 elements */
+  int64_t swa_rows;
+  const void* compressed_pool; /* [compressed_rows, row_stride]; may be NULL
+                                  only if K <= 128 */
+  int64_t compressed_rows;
+  int32_t kv_dtype;            /* dtype of both pools */
+  int32_t flags;               /* SMLA_FLAG_* */
+  int64_t pool_row_stride;     /* elements between rows of both pools; 0 means
+                                  512.  A pool of one KV head is the same
+                                  bytes in HND and NHD layouts, so a paged
+                                  [pages, page_size, 512] pool is passed as
+                                  flat rows row = page * page_size + offset */
+  const int32_t* indices;      /* [T, index_row_stride], first K columns used */
+  int64_t index_row_stride;    /* 0 means K */
+  const int32_t* topk_lens;    /* [T] active column count (<= K) or NULL = K */
+  const int32_t* seq_lens;     /* [num_requests] or NULL; accepted, unused by the math */
+  const int32_t* cum_seq_lens_q; /* [num_requests + 1] or NULL; accepted, unused by the math */
+  int32_t num_requests;
+  int32_t reserved0;
+  const float* sinks;          /* [H] fp32 or NULL */
+  float bmm1_scale;            /* QK scale: sm_scale (* q_scale * kv_scale for FP8) */
+  float bmm2_scale;            /* VO scale: 1 (or kv_scale for FP8 pools) */
+  float lse_scale;             /* multiplier of the base-2 LSE, 1 by default */
+  int32_t reserved1;
+  void* out;                   /* [T, H, 512] BF16 contiguous, 16-B aligned */
+  float* out_lse;              /* [T, H] fp32 or NULL */
+  void* workspace;             /* device scratch, 256-B aligned; may be NULL
+                                  when sparse_mla_workspace_size() is 0 */
+  size_t workspace_bytes;
+} smla_decode_args;
+
+/* Choose the split-K plan from shapes only (host-only, deterministic, no
+ * device work; FlashInfer cake_* "num_splits"/"max_splits" and the adaptive
+ * chunking of msa_sparse_decode_attention "force_fused": one chunk per
+ * block at low batch, a single chunk at high batch).
+ *   max_splits <= 0 selects the default cap 16; num_splits_override > 0
+ *   forces S = clamp(override, 1, min(num_chunks, SMLA_MAX_SPLITS));
+ *   num_cus <= 0 queries the current device's compute-unit count once and
+ *   caches it per device.
+ * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1 or a NULL out_plan,
+ * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128}, SMLA_ERR_HIP if the
+ * device query fails. */
+int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
+                           int max_splits, int num_splits_override,
+                           int num_cus, smla_plan* out_plan);
+
+/* Workspace bytes sparse_mla_decode needs for this plan: a 256-B error
+ * block, then (when S > 1) mid_lse [T, H, S] fp32 and mid_out
+ * [T, H, S, 512] BF16 (FlashInfer cake_* "mid_out"/"mid_lse").  Returns 0
+ * when S == 1 and validation is off (pass flags), or (size_t)-1 on bad
+ * arguments. */
+size_t sparse_mla_workspace_size(const smla_plan* plan, int T, int H,
+                                 int flags);
+
+/* Byte offsets of mid_lse and mid_out inside a workspace laid out for
+ * (plan, T, H); for callers that want to inspect the partials. */
+int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
+                                size_t* mid_lse_offset,
+                                size_t* mid_out_offset);
+
+/* Run the decode asynchronously on "stream": the split kernel, then the
+ * combine kernel when plan->num_splits > 1.  plan == NULL plans
+ * internally (defaults, current device).  No allocation and no
+ * synchronisation, so the call can be captured into a HIP graph (FlashInfer
+ * msa_sparse_decode_attention "workspace": host arithmetic only before the
+ * launches).  Alignment rules (SMLA_ERR_MISALIGNED): q, out, both pools
+ * and pool_row_stride * element size are multiples of 16 bytes; the
+ * workspace is 256-B aligned.  Indices at columns >= topk_lens[t] are
+ * never read as rows. */
+int sparse_mla_decode(const smla_decode_args* args, const smla_plan* plan,
+                      smla_stream_t stream);
+
+/* Merge split partials (FlashInfer cake_* "mid_out"/"mid_lse" and the
+ * combine of msa_sparse_decode_attention "force_fused"):
+ *   mid_out [T, H, split_stride, 512] BF16 and mid_lse [T, H, split_stride]
+ *   fp32 hold, for splits s < S, a normalised partial output (bmm2 already
+ *   applied) and its base-2 LSE without sink or lse_scale (-inf = empty).
+ *   out [T, H, 512] BF16 and out_lse [T, H] (or NULL) receive the merge,
+ *   with the sink (if sinks != NULL) added once.
+ * 1 <= S <= split_stride, S <= SMLA_MAX_SPLITS, H in {64,128}. */
+int sparse_mla_combine(const void* mid_out, const float* mid_lse, int T,
+                       int H, int S, int split_stride, const float* sinks,
+                       float lse_scale, void* out, float* out_lse,
+                       smla_stream_t stream);
+
+/* Read the device error block of a workspace used with
+ * SMLA_FLAG_VALIDATE_INDICES.  SYNCHRONISES "stream".  *code receives an
+ * SMLA_DEVERR_* value, *token and *column the first violation found (or
+ * -1).  Any of the output pointers may be NULL. */
+int sparse_mla_get_device_error(const void* workspace, smla_stream_t stream,
+                                int32_t* code, int32_t* token,
+                                int32_t* column);
+
+/* Static description of a status code. */
+const char* sparse_mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSEMLA_H_ */

@@ -1,0 +1,312 @@
+// C-ABI of libsparsemla: argument validation, the split-K planner,
+// workspace carving and kernel launches.  Host code only; everything here
+// is shape arithmetic, so a call costs no device synchronisation and can be
+// captured into a HIP graph.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "internal.h"
+#include "sparsemla.h"
+
+namespace {
+
+constexpr int kDefaultMaxSplits = 16;   // FlashInfer cake_* default max_splits
+constexpr int kChunkCols = 64;          // split granularity in table columns
+
+// Cost model constants, in units of "one gathered 1 KB row" of one
+// workgroup's time: fixed per-workgroup cost (Q load, compaction,
+// epilogue) and the combine launch.
+constexpr int64_t kWgOverheadRows = 96;
+constexpr int64_t kCombineLaunchRows = 32;
+
+std::mutex g_cu_mutex;
+int g_cu_count[64] = {0};
+
+int query_cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return SMLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (dev < 64 && g_cu_count[dev] > 0) {
+    *out = g_cu_count[dev];
+    return SMLA_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+          hipSuccess ||
+      n <= 0)
+    return SMLA_ERR_HIP;
+  if (dev < 64) g_cu_count[dev] = n;
+  *out = n;
+  return SMLA_OK;
+}
+
+bool dtype_pair_ok(int q, int kv) {
+  if (q == SMLA_DTYPE_BF16 && kv == SMLA_DTYPE_BF16) return true;
+  if (q == SMLA_DTYPE_FP8_E4M3FN && kv == SMLA_DTYPE_FP8_E4M3FN) return true;
+  if (q == SMLA_DTYPE_BF16 && kv == SMLA_DTYPE_FP8_E4M3FN) return true;
+  return false;
+}
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct Layout {
+  size_t mid_lse, mid_out, total;
+};
+
+Layout layout_for(int S, int T, int H, int flags) {
+  Layout L{0, 0, 0};
+  if (S <= 1) {
+    L.total = (flags & SMLA_FLAG_VALIDATE_INDICES) ? smla::kErrBlockBytes : 0;
+    return L;
+  }
+  L.mid_lse = smla::kErrBlockBytes;
+  const size_t lse_bytes = (size_t)T * H * S * sizeof(float);
+  L.mid_out = round_up(L.mid_lse + lse_bytes, 256);
+  L.total = L.mid_out + (size_t)T * H * S * smla::kHeadDim * 2;
+  return L;
+}
+
+bool plan_ok(const smla_plan* p, int K) {
+  if (p->num_splits < 1 || p->num_splits > SMLA_MAX_SPLITS) return false;
+  if (p->chunk_cols < 1 || p->chunks_per_split < 1) return false;
+  if (p->K != K) return false;
+  const int64_t cover = (int64_t)p->num_splits * p->chunks_per_split * p->chunk_cols;
+  return cover >= K;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
+                           int max_splits, int num_splits_override,
+                           int num_cus, smla_plan* out_plan) {
+  if (!out_plan || T < 0 || K < 1) return SMLA_ERR_INVALID_ARG;
+  if (H != 64 && H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
+  if (!dtype_pair_ok(q_dtype, kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
+  if (num_cus <= 0) {
+    const int st = query_cu_count(&num_cus);
+    if (st != SMLA_OK) return st;
+  }
+  const int num_chunks = (K + kChunkCols - 1) / kChunkCols;
+  int cap = max_splits > 0 ? max_splits : kDefaultMaxSplits;
+  cap = std::min(std::min(cap, num_chunks), SMLA_MAX_SPLITS);
+
+  int S = 1;
+  if (num_splits_override > 0) {
+    S = std::min(std::max(num_splits_override, 1),
+                 std::min(num_chunks, SMLA_MAX_SPLITS));
+  } else if (T > 0) {
+    // Workgroups resident per CU: one at H=128 (it holds 32 heads of O per
+    // wave in registers), two at H=64.
+    const int64_t slots = (int64_t)num_cus * (H == 64 ? 2 : 1);
+    // Per-row cost relative to a BF16 row: FP8 rows move half the bytes.
+    const int64_t row_w = (kv_dtype == SMLA_DTYPE_FP8_E4M3FN) ? 1 : 2;
+    int64_t best = INT64_MAX;
+    for (int s = 1; s <= cap; ++s) {
+      const int64_t cps = (num_chunks + s - 1) / s;
+      const int64_t rows = std::min<int64_t>(cps * kChunkCols, K);
+      const int64_t waves = ((int64_t)T * s + slots - 1) / slots;
+      // a split writes a BF16 partial of H rows-worth of bytes
+      const int64_t per_wg = 2 * kWgOverheadRows + rows * row_w +
+                             (s > 1 ? 2 * (int64_t)H : 0);
+      int64_t cost = waves * per_wg;
+      if (s > 1)
+        cost += 2 * kCombineLaunchRows +
+                (2 * (int64_t)T * H * s + num_cus - 1) / num_cus;
+      if (cost < best) {
+        best = cost;
+        S = s;
+      }
+    }
+  }
+  const int cps = (num_chunks + S - 1) / S;
+  out_plan->num_splits = S;
+  out_plan->head_tiles = 1;
+  out_plan->chunk_cols = kChunkCols;
+  out_plan->chunks_per_split = cps;
+  out_plan->num_chunks = num_chunks;
+  out_plan->K = K;
+  out_plan->reserved[0] = out_plan->reserved[1] = 0;
+  return SMLA_OK;
+}
+
+size_t sparse_mla_workspace_size(const smla_plan* plan, int T, int H,
+                                 int flags) {
+  if (!plan || T < 0 || (H != 64 && H != 128) || plan->num_splits < 1)
+    return (size_t)-1;
+  return layout_for(plan->num_splits, T, H, flags).total;
+}
+
+int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
+                                size_t* mid_lse_offset,
+                                size_t* mid_out_offset) {
+  if (!plan || T < 0 || (H != 64 && H != 128) || plan->num_splits < 1)
+    return SMLA_ERR_INVALID_ARG;
+  const Layout L = layout_for(plan->num_splits, T, H, 0);
+  if (mid_lse_offset) *mid_lse_offset = L.mid_lse;
+  if (mid_out_offset) *mid_out_offset = L.mid_out;
+  return SMLA_OK;
+}
+
+int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
+                      smla_stream_t stream_handle) {
+  if (!a) return SMLA_ERR_INVALID_ARG;
+  if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
+  if (a->H != 64 && a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
+  if (!dtype_pair_ok(a->q_dtype, a->kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
+  if (a->T == 0) return SMLA_OK;
+  if (!a->q || !a->swa_pool || !a->indices || !a->out) return SMLA_ERR_INVALID_ARG;
+  if (a->K > smla::kSwaColumns && !a->compressed_pool) return SMLA_ERR_INVALID_ARG;
+  if (a->swa_rows < 0 || a->compressed_rows < 0) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)a->T * a->H > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
+  const int64_t row_stride = a->pool_row_stride == 0 ? smla::kHeadDim : a->pool_row_stride;
+  if (row_stride < smla::kHeadDim) return SMLA_ERR_INVALID_ARG;
+  const int64_t idx_stride = a->index_row_stride == 0 ? a->K : a->index_row_stride;
+  if (idx_stride < a->K) return SMLA_ERR_INVALID_ARG;
+  if (a->cum_seq_lens_q && a->num_requests < 1) return SMLA_ERR_INVALID_ARG;
+  const int kv_elem = a->kv_dtype == SMLA_DTYPE_FP8_E4M3FN ? 1 : 2;
+  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->swa_pool, 16) ||
+      (a->compressed_pool && !aligned(a->compressed_pool, 16)) ||
+      (row_stride * kv_elem) % 16 != 0 || !aligned(a->indices, 4))
+    return SMLA_ERR_MISALIGNED;
+
+  smla_plan local;
+  if (!plan) {
+    const int st = sparse_mla_plan_splits(a->T, a->H, a->K, a->q_dtype, a->kv_dtype,
+                                          0, 0, 0, &local);
+    if (st != SMLA_OK) return st;
+    plan = &local;
+  }
+  if (!plan_ok(plan, a->K)) return SMLA_ERR_BAD_PLAN;
+  const int S = plan->num_splits;
+  if ((int64_t)a->T * S > INT_MAX) return SMLA_ERR_INVALID_ARG;
+
+  const bool validate = (a->flags & SMLA_FLAG_VALIDATE_INDICES) != 0;
+  const Layout L = layout_for(S, a->T, a->H, a->flags);
+  if (L.total > 0) {
+    if (!a->workspace) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    if (a->workspace_bytes < L.total) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(a->workspace, 256)) return SMLA_ERR_MISALIGNED;
+  }
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
+  uint8_t* ws = static_cast<uint8_t*>(a->workspace);
+  int32_t* err = validate ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  if (validate && smla::launch_clear_error(err, stream) != hipSuccess)
+    return SMLA_ERR_HIP;
+
+  smla::DecodeParams p{};
+  p.q = a->q;
+  p.swa = static_cast<const uint8_t*>(a->swa_pool);
+  p.comp = static_cast<const uint8_t*>(a->compressed_pool);
+  p.swa_rows = a->swa_rows;
+  p.comp_rows = a->compressed_pool ? a->compressed_rows : 0;
+  p.row_stride_bytes = row_stride * kv_elem;
+  p.indices = a->indices;
+  p.index_row_stride = idx_stride;
+  p.topk_lens = a->topk_lens;
+  p.sinks = a->sinks;
+  p.scale_log2 = (float)((double)a->bmm1_scale * 1.4426950408889634);
+  p.bmm2 = a->bmm2_scale;
+  p.lse_scale = a->lse_scale;
+  p.out = a->out;
+  p.out_lse = a->out_lse;
+  p.err = err;
+  p.T = a->T;
+  p.H = a->H;
+  p.K = a->K;
+  p.S = S;
+  p.split_cols = plan->chunks_per_split * plan->chunk_cols;
+  p.validate = validate ? 1 : 0;
+  if (S > 1) {
+    p.mid_lse = reinterpret_cast<float*>(ws + L.mid_lse);
+    p.mid_out = reinterpret_cast<uint16_t*>(ws + L.mid_out);
+  }
+  if (smla::launch_decode(p, a->q_dtype, a->kv_dtype, stream) != hipSuccess)
+    return SMLA_ERR_HIP;
+  if (S > 1) {
+    smla::CombineParams c{};
+    c.mid_out = p.mid_out;
+    c.mid_lse = p.mid_lse;
+    c.sinks = a->sinks;
+    c.lse_scale = a->lse_scale;
+    c.out = static_cast<uint16_t*>(a->out);
+    c.out_lse = a->out_lse;
+    c.T = a->T;
+    c.H = a->H;
+    c.S = S;
+    c.stride = S;
+    if (smla::launch_combine(c, stream) != hipSuccess) return SMLA_ERR_HIP;
+  }
+  return SMLA_OK;
+}
+
+int sparse_mla_combine(const void* mid_out, const float* mid_lse, int T, int H,
+                       int S, int split_stride, const float* sinks,
+                       float lse_scale, void* out, float* out_lse,
+                       smla_stream_t stream_handle) {
+  if (T < 0 || S < 1 || S > SMLA_MAX_SPLITS || split_stride < S)
+    return SMLA_ERR_INVALID_ARG;
+  if (H != 64 && H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
+  if (T == 0) return SMLA_OK;
+  if (!mid_out || !mid_lse || !out) return SMLA_ERR_INVALID_ARG;
+  if (!aligned(mid_out, 16) || !aligned(out, 16) || !aligned(mid_lse, 4))
+    return SMLA_ERR_MISALIGNED;
+  smla::CombineParams c{};
+  c.mid_out = static_cast<const uint16_t*>(mid_out);
+  c.mid_lse = mid_lse;
+  c.sinks = sinks;
+  c.lse_scale = lse_scale;
+  c.out = static_cast<uint16_t*>(out);
+  c.out_lse = out_lse;
+  c.T = T;
+  c.H = H;
+  c.S = S;
+  c.stride = split_stride;
+  if (smla::launch_combine(c, reinterpret_cast<hipStream_t>(stream_handle)) !=
+      hipSuccess)
+    return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
+int sparse_mla_get_device_error(const void* workspace, smla_stream_t stream_handle,
+                                int32_t* code, int32_t* token, int32_t* column) {
+  if (!workspace) return SMLA_ERR_INVALID_ARG;
+  int32_t host[4] = {0, -1, -1, 0};
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
+  if (hipMemcpyAsync(host, workspace, sizeof(host), hipMemcpyDeviceToHost, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SMLA_ERR_HIP;
+  if (code) *code = host[0];
+  if (token) *token = host[1];
+  if (column) *column = host[2];
+  return SMLA_OK;
+}
+
+const char* sparse_mla_status_string(int status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_INVALID_ARG: return "invalid argument";
+    case SMLA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype pair";
+    case SMLA_ERR_UNSUPPORTED_SHAPE: return "unsupported shape (H must be 64 or 128)";
+    case SMLA_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or too small";
+    case SMLA_ERR_MISALIGNED: return "misaligned pointer or stride";
+    case SMLA_ERR_BAD_PLAN: return "plan inconsistent with the call";
+    case SMLA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (api.cpp) and the gfx950
+// kernels (kernels.hip).  Not installed; not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kHeadDim = 512;
+constexpr int kSwaColumns = 128;
+constexpr int kMaxSplits = 64;
+constexpr int kErrBlockBytes = 256;
+
+// Everything the split kernel needs, resolved on the host.
+struct DecodeParams {
+  const void* q;                 // [T, H, 512]
+  const uint8_t* swa;            // pool base pointers (bytes)
+  const uint8_t* comp;
+  int64_t swa_rows;
+  int64_t comp_rows;
+  int64_t row_stride_bytes;      // bytes between consecutive pool rows
+  const int32_t* indices;
+  int64_t index_row_stride;      // elements
+  const int32_t* topk_lens;      // may be null
+  const float* sinks;            // may be null
+  float scale_log2;              // bmm1_scale * log2(e)
+  float bmm2;
+  float lse_scale;
+  void* out;                     // bf16 [T, H, 512]      (S == 1)
+  float* out_lse;                // [T, H] or null        (S == 1)
+  uint16_t* mid_out;             // bf16 [T, H, S, 512]   (S > 1)
+  float* mid_lse;                // [T, H, S]             (S > 1)
+  int32_t* err;                  // error block or null
+  int32_t T, H, K, S;
+  int32_t split_cols;            // columns per split
+  int32_t validate;
+};
+
+struct CombineParams {
+  const uint16_t* mid_out;       // bf16 [T, H, stride, 512]
+  const float* mid_lse;          // [T, H, stride]
+  const float* sinks;            // [H] or null
+  float lse_scale;
+  uint16_t* out;                 // bf16 [T, H, 512]
+  float* out_lse;                // [T, H] or null
+  int32_t T, H, S, stride;
+};
+
+hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
+                         hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
+
+}  // namespace smla

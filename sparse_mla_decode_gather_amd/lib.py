@@ -1,0 +1,287 @@
+"""ctypes binding of libsparsemla (``include/sparsemla.h``).
+
+Argument marshalling only: tensors become device pointers, dtypes become the
+library's enums, torch's current HIP stream is passed through.  Every step
+of the decode runs in the library's HIP kernels; nothing here computes.  If
+the shared library is missing this module raises instead of falling back.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+from .build import LIB_PATH, INCLUDE
+
+SMLA_OK = 0
+STATUS = {
+    0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED_DTYPE",
+    3: "SMLA_ERR_UNSUPPORTED_SHAPE", 4: "SMLA_ERR_WORKSPACE_TOO_SMALL",
+    5: "SMLA_ERR_MISALIGNED", 6: "SMLA_ERR_BAD_PLAN", 7: "SMLA_ERR_HIP",
+}
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3FN = 1
+FLAG_VALIDATE_INDICES = 1
+DEVERR = {0: "none", 1: "index out of range", 2: "topk_len out of range"}
+
+
+class SparseMLAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} "
+                         f"({_status_string(status)})")
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("num_splits", ctypes.c_int32), ("head_tiles", ctypes.c_int32),
+                ("chunk_cols", ctypes.c_int32),
+                ("chunks_per_split", ctypes.c_int32),
+                ("num_chunks", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
+
+    def as_dict(self):
+        return {"num_splits": self.num_splits, "head_tiles": self.head_tiles,
+                "chunk_cols": self.chunk_cols,
+                "chunks_per_split": self.chunks_per_split,
+                "num_chunks": self.num_chunks, "K": self.K}
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("H", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("q_dtype", ctypes.c_int32), ("q", ctypes.c_void_p),
+        ("swa_pool", ctypes.c_void_p), ("swa_rows", ctypes.c_int64),
+        ("compressed_pool", ctypes.c_void_p),
+        ("compressed_rows", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
+        ("flags", ctypes.c_int32), ("pool_row_stride", ctypes.c_int64),
+        ("indices", ctypes.c_void_p), ("index_row_stride", ctypes.c_int64),
+        ("topk_lens", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("cum_seq_lens_q", ctypes.c_void_p), ("num_requests", ctypes.c_int32),
+        ("reserved0", ctypes.c_int32), ("sinks", ctypes.c_void_p),
+        ("bmm1_scale", ctypes.c_float), ("bmm2_scale", ctypes.c_float),
+        ("lse_scale", ctypes.c_float), ("reserved1", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("out_lse", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libsparsemla.so from the package directory (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing; build it first "
+            "(python -m sparse_mla_decode_gather_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    lib.sparse_mla_plan_splits.argtypes = [ctypes.c_int] * 8 + [
+        ctypes.POINTER(Plan)]
+    lib.sparse_mla_plan_splits.restype = ctypes.c_int
+    lib.sparse_mla_workspace_size.argtypes = [ctypes.POINTER(Plan), ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+    lib.sparse_mla_workspace_size.restype = ctypes.c_size_t
+    lib.sparse_mla_workspace_layout.argtypes = [
+        ctypes.POINTER(Plan), ctypes.c_int, ctypes.c_int,
+        ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+    lib.sparse_mla_workspace_layout.restype = ctypes.c_int
+    lib.sparse_mla_decode.argtypes = [ctypes.POINTER(DecodeArgs),
+                                      ctypes.POINTER(Plan), ctypes.c_void_p]
+    lib.sparse_mla_decode.restype = ctypes.c_int
+    lib.sparse_mla_combine.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.sparse_mla_combine.restype = ctypes.c_int
+    lib.sparse_mla_get_device_error.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
+        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    lib.sparse_mla_get_device_error.restype = ctypes.c_int
+    lib.sparse_mla_status_string.argtypes = [ctypes.c_int]
+    lib.sparse_mla_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions include/sparsemla.h declares."""
+    with open(os.path.join(INCLUDE, "sparsemla.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_mla_[a-z_]+)\s*\(", text)))
+
+
+def _status_string(status: int) -> str:
+    try:
+        return load().sparse_mla_status_string(status).decode()
+    except Exception:          # the library itself may be what is missing
+        return "?"
+
+
+def _check(status: int, where: str):
+    if status != SMLA_OK:
+        raise SparseMLAError(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float8_e4m3fn:
+        return DTYPE_FP8_E4M3FN
+    raise TypeError(f"unsupported element type {t.dtype}")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+
+def plan_splits(T: int, H: int, K: int, q_dtype: int = DTYPE_BF16,
+                kv_dtype: int = DTYPE_BF16, max_splits: int = 0,
+                num_splits: int = 0, num_cus: int = 0) -> Plan:
+    plan = Plan()
+    _check(load().sparse_mla_plan_splits(T, H, K, q_dtype, kv_dtype, max_splits,
+                                         num_splits, num_cus,
+                                         ctypes.byref(plan)),
+           "sparse_mla_plan_splits")
+    return plan
+
+
+def workspace_size(plan: Plan, T: int, H: int, flags: int = 0) -> int:
+    n = load().sparse_mla_workspace_size(ctypes.byref(plan), T, H, flags)
+    if n == ctypes.c_size_t(-1).value:
+        raise SparseMLAError(1, "sparse_mla_workspace_size")
+    return int(n)
+
+
+def workspace_layout(plan: Plan, T: int, H: int):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load().sparse_mla_workspace_layout(ctypes.byref(plan), T, H,
+                                              ctypes.byref(a), ctypes.byref(b)),
+           "sparse_mla_workspace_layout")
+    return int(a.value), int(b.value)
+
+
+def alloc_workspace(plan: Plan, T: int, H: int, flags: int = 0,
+                    device="cuda") -> Optional[torch.Tensor]:
+    """A device byte buffer of the size the plan needs (None if zero).
+    torch's caching allocator returns 256-B aligned storage."""
+    n = workspace_size(plan, T, H, flags)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def make_args(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
+              topk_lens=None, seq_lens=None, cum_seq_lens_q=None, sinks=None,
+              bmm1_scale=1.0, bmm2_scale=1.0, lse_scale=1.0, workspace=None,
+              flags=0, pool_row_stride=0) -> DecodeArgs:
+    a = DecodeArgs()
+    T, H = int(q.shape[0]), int(q.shape[1])
+    a.T, a.H, a.K = T, H, int(indices.shape[1])
+    a.q_dtype = dtype_code(q)
+    a.q = _ptr(q)
+    a.swa_pool = _ptr(swa_pool)
+    a.swa_rows = int(swa_pool.shape[0])
+    a.compressed_pool = _ptr(compressed_pool)
+    a.compressed_rows = 0 if compressed_pool is None else int(
+        compressed_pool.shape[0])
+    a.kv_dtype = dtype_code(swa_pool)
+    a.flags = flags
+    a.pool_row_stride = pool_row_stride or int(swa_pool.stride(0))
+    a.indices = _ptr(indices)
+    a.index_row_stride = int(indices.stride(0))
+    a.topk_lens = _ptr(topk_lens)
+    a.seq_lens = _ptr(seq_lens)
+    a.cum_seq_lens_q = _ptr(cum_seq_lens_q)
+    a.num_requests = 0 if seq_lens is None else int(seq_lens.numel())
+    a.sinks = _ptr(sinks)
+    a.bmm1_scale, a.bmm2_scale, a.lse_scale = bmm1_scale, bmm2_scale, lse_scale
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * \
+        workspace.element_size()
+    return a
+
+
+def decode(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
+           topk_lens=None, seq_lens=None, cum_seq_lens_q=None, sinks=None,
+           bmm1_scale=1.0, bmm2_scale=1.0, lse_scale=1.0, workspace=None,
+           plan: Optional[Plan] = None, flags=0, stream=None) -> Plan:
+    """sparse_mla_decode: writes ``out`` (and ``out_lse``) in place on the
+    current (or given) stream and returns the plan used.  With no workspace
+    given, one of the size the plan needs is allocated (device memory only).
+    """
+    T, H, K = int(q.shape[0]), int(q.shape[1]), int(indices.shape[1])
+    if plan is None:
+        plan = plan_splits(T, H, K, dtype_code(q), dtype_code(swa_pool))
+    if workspace is None:
+        workspace = alloc_workspace(plan, T, H, flags, q.device)
+    args = make_args(q, swa_pool, compressed_pool, indices, out,
+                     out_lse=out_lse, topk_lens=topk_lens, seq_lens=seq_lens,
+                     cum_seq_lens_q=cum_seq_lens_q, sinks=sinks,
+                     bmm1_scale=bmm1_scale, bmm2_scale=bmm2_scale,
+                     lse_scale=lse_scale, workspace=workspace, flags=flags)
+    _check(load().sparse_mla_decode(ctypes.byref(args), ctypes.byref(plan),
+                                    _stream(stream)), "sparse_mla_decode")
+    return plan
+
+
+def combine(mid_out, mid_lse, S: int, out, *, out_lse=None, sinks=None,
+            lse_scale=1.0, stream=None):
+    """sparse_mla_combine over mid_out [T,H,stride,512] / mid_lse
+    [T,H,stride] (first S splits)."""
+    T, H, stride = (int(x) for x in mid_lse.shape)
+    _check(load().sparse_mla_combine(_ptr(mid_out), _ptr(mid_lse), T, H, S,
+                                     stride, _ptr(sinks), lse_scale, _ptr(out),
+                                     _ptr(out_lse), _stream(stream)),
+           "sparse_mla_combine")
+
+
+def get_device_error(workspace, stream=None):
+    """sparse_mla_get_device_error (synchronises): (code, token, column)."""
+    c, t, col = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    _check(load().sparse_mla_get_device_error(_ptr(workspace), _stream(stream),
+                                              ctypes.byref(c), ctypes.byref(t),
+                                              ctypes.byref(col)),
+           "sparse_mla_get_device_error")
+    return int(c.value), int(t.value), int(col.value)
+
+
+def status_string(status: int) -> str:
+    return load().sparse_mla_status_string(status).decode()
+
+
+def decode_workload(w, out=None, out_lse=None, plan=None, flags=0,
+                    workspace=None, stream=None):
+    """Run sparse_mla_decode on a ``workloads.Workload`` resident on the GPU."""
+    if out is None:
+        out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16,
+                          device=w.q.device)
+    if out_lse is None:
+        out_lse = torch.empty((w.T, w.H), dtype=torch.float32,
+                              device=w.q.device)
+    plan = decode(w.q, w.swa_pool, w.comp_pool, w.indices, out,
+                  out_lse=out_lse, topk_lens=w.topk_lens, seq_lens=w.seq_lens,
+                  cum_seq_lens_q=w.cum_seq_lens_q, sinks=w.sinks,
+                  bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                  lse_scale=w.lse_scale, workspace=workspace, plan=plan,
+                  flags=flags, stream=stream)
+    return out, out_lse, plan

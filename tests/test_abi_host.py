@@ -1,0 +1,227 @@
+"""The C-ABI library on the host (CPU only, no kernel is ever launched).
+
+Covers: the library loads and exports every function include/sparsemla.h
+declares; status strings; the split planner's bounds and determinism;
+workspace sizing; and every host-side argument check of sparse_mla_decode /
+sparse_mla_combine.  The argument checks use non-null dummy pointer values
+with exactly one violation each, so every call is rejected before anything
+would be launched.
+"""
+
+import ctypes
+import json
+import os
+
+import pytest
+
+from sparse_mla_decode_gather_amd import lib as L
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden",
+                      "pages_constants.json")
+
+
+@pytest.fixture(scope="module")
+def so():
+    return L.load()
+
+
+def test_every_declared_symbol_is_exported(so):
+    names = L.header_functions()
+    assert set(names) == {
+        "sparse_mla_plan_splits", "sparse_mla_workspace_size",
+        "sparse_mla_workspace_layout", "sparse_mla_decode",
+        "sparse_mla_combine", "sparse_mla_get_device_error",
+        "sparse_mla_status_string"}
+    for n in names:
+        assert hasattr(so, n), n
+
+
+def test_status_strings(so):
+    for code in range(8):
+        assert L.status_string(code) not in ("", "unknown status")
+    assert L.status_string(99) == "unknown status"
+
+
+def test_pages_constants_match_header():
+    with open(os.path.join(L.INCLUDE, "sparsemla.h")) as f:
+        hdr = f.read()
+    c = json.load(open(GOLDEN))
+    assert f"SMLA_SWA_COLUMNS  {c['swa_columns']['value']}" in hdr
+    assert f"SMLA_HEAD_DIM     {c['head_dim']['value']}" in hdr
+
+
+# ---------------------------------------------------------------------------
+# planner
+# ---------------------------------------------------------------------------
+
+def plan(T, H=128, K=2048, q=0, kv=0, max_splits=0, override=0, cus=256):
+    return L.plan_splits(T, H, K, q, kv, max_splits, override, cus)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 64, 100, 256, 300, 512, 4096])
+@pytest.mark.parametrize("H,K", [(128, 2048), (64, 1024), (128, 512), (64, 256),
+                                 (128, 100), (64, 5000)])
+def test_plan_bounds(T, H, K):
+    p = plan(T, H, K)
+    assert 1 <= p.num_splits <= 16 and p.num_splits <= p.num_chunks
+    assert p.head_tiles == 1 and p.K == K
+    assert p.num_chunks == -(-K // p.chunk_cols)
+    assert p.num_splits * p.chunks_per_split * p.chunk_cols >= K
+    # no split is entirely past the table
+    assert (p.num_splits - 1) * p.chunks_per_split * p.chunk_cols < K
+    q = plan(T, H, K)
+    assert p.as_dict() == q.as_dict()
+
+
+def test_plan_adapts_to_batch():
+    # one chunk per block at low batch, a single chunk at high batch
+    assert plan(1).num_splits == 16
+    assert plan(8).num_splits == 16
+    assert plan(512).num_splits == 1
+    assert plan(4096).num_splits == 1
+    assert plan(1, max_splits=4).num_splits == 4
+
+
+def test_plan_override_and_clamp():
+    assert plan(512, override=3).num_splits == 3
+    assert plan(512, K=100, override=16).num_splits == 2   # only 2 chunks
+    assert plan(1, K=64 * 64, override=1000).num_splits == 64
+
+
+@pytest.mark.parametrize("args,code", [
+    ((-1, 128, 2048), 1), ((4, 128, 0), 1), ((4, 96, 2048), 3),
+    ((4, 256, 2048), 3),
+])
+def test_plan_rejects(args, code, so):
+    p = L.Plan()
+    assert so.sparse_mla_plan_splits(*args, 0, 0, 0, 0, 256,
+                                     ctypes.byref(p)) == code
+    assert so.sparse_mla_plan_splits(4, 128, 2048, 1, 0, 0, 0, 256,
+                                     ctypes.byref(p)) == 2   # FP8 q, BF16 KV
+
+
+def test_workspace_sizes():
+    p1 = plan(512)
+    assert L.workspace_size(p1, 512, 128) == 0
+    assert L.workspace_size(p1, 512, 128, L.FLAG_VALIDATE_INDICES) == 256
+    p = plan(8)
+    S = p.num_splits
+    lse_off, out_off = L.workspace_layout(p, 8, 128)
+    assert lse_off == 256 and out_off % 256 == 0
+    assert out_off >= lse_off + 8 * 128 * S * 4
+    assert L.workspace_size(p, 8, 128) == out_off + 8 * 128 * S * 512 * 2
+
+
+# ---------------------------------------------------------------------------
+# argument validation of sparse_mla_decode (rejected before any launch)
+# ---------------------------------------------------------------------------
+
+DUMMY = 0x7f0000000000      # 256-B aligned, never dereferenced
+
+
+def good_args(T=4, H=128, K=256):
+    a = L.DecodeArgs()
+    a.T, a.H, a.K = T, H, K
+    a.q_dtype = a.kv_dtype = 0
+    a.q = a.swa_pool = a.compressed_pool = a.out = DUMMY
+    a.indices = DUMMY
+    a.swa_rows, a.compressed_rows = 1024, 4096
+    a.bmm1_scale, a.bmm2_scale, a.lse_scale = 0.04, 1.0, 1.0
+    return a
+
+
+def call(so, a, p=None, T=None):
+    if p is None:
+        p = plan(max(a.T if T is None else T, 1),
+                 a.H if a.H in (64, 128) else 128, max(a.K, 1))
+    return so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("T", -1, 1), ("K", 0, 1), ("H", 96, 3), ("H", 256, 3),
+    ("q", None, 1), ("swa_pool", None, 1), ("indices", None, 1),
+    ("out", None, 1), ("compressed_pool", None, 1),
+    ("swa_rows", -5, 1), ("q_dtype", 1, 2), ("kv_dtype", 2, 2),
+    ("q", DUMMY + 8, 5), ("out", DUMMY + 2, 5), ("swa_pool", DUMMY + 4, 5),
+    ("compressed_pool", DUMMY + 8, 5), ("indices", DUMMY + 2, 5),
+    ("pool_row_stride", 500, 1), ("pool_row_stride", 516, 5),
+    ("index_row_stride", 100, 1), ("cum_seq_lens_q", DUMMY, 1),
+])
+def test_decode_rejects(so, field, value, code):
+    a = good_args()
+    setattr(a, field, value)
+    assert call(so, a) == code
+
+
+def test_decode_null_args_and_empty_batch(so):
+    assert so.sparse_mla_decode(None, None, None) == 1
+    a = good_args(T=0)
+    a.q = a.out = None         # nothing is touched for T = 0
+    p = plan(1, 128, 256)
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 0
+
+
+def test_decode_swa_only_allows_null_compressed_pool(so):
+    a = good_args(K=128)
+    a.compressed_pool = None
+    a.workspace = None
+    p = plan(4, 128, 128)
+    # the only thing left to fail is a plan mismatch, which we force here
+    p.K = 64
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 6
+
+
+def test_decode_workspace_checks(so):
+    a = good_args(T=8, K=2048)
+    p = plan(8, 128, 2048)
+    assert p.num_splits > 1
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 4
+    a.workspace = DUMMY
+    a.workspace_bytes = L.workspace_size(p, 8, 128) - 1
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 4
+    a.workspace_bytes += 1
+    a.workspace = DUMMY + 128
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 5
+    # validation needs the error block even without splits
+    a = good_args(T=512, K=2048)
+    a.flags = L.FLAG_VALIDATE_INDICES
+    p = plan(512, 128, 2048)
+    assert p.num_splits == 1
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 4
+
+
+@pytest.mark.parametrize("mutate", [
+    lambda p: setattr(p, "num_splits", 0),
+    lambda p: setattr(p, "num_splits", 65),
+    lambda p: setattr(p, "chunk_cols", 0),
+    lambda p: setattr(p, "K", 999),
+    lambda p: setattr(p, "chunks_per_split", 1),   # no longer covers K
+])
+def test_decode_rejects_bad_plan(so, mutate):
+    a = good_args(T=4, K=2048)
+    p = plan(512, 128, 2048)
+    mutate(p)
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 6
+
+
+@pytest.mark.parametrize("args,code", [
+    ((4, 128, 0, 4), 1), ((4, 128, 65, 65), 1), ((4, 128, 4, 3), 1),
+    ((4, 96, 4, 4), 3), ((-1, 128, 4, 4), 1),
+])
+def test_combine_rejects(so, args, code):
+    T, H, S, stride = args
+    assert so.sparse_mla_combine(DUMMY, DUMMY, T, H, S, stride, None, 1.0,
+                                 DUMMY, None, None) == code
+
+
+def test_combine_rejects_null_and_misaligned(so):
+    assert so.sparse_mla_combine(None, DUMMY, 4, 128, 2, 2, None, 1.0, DUMMY,
+                                 None, None) == 1
+    assert so.sparse_mla_combine(DUMMY + 8, DUMMY, 4, 128, 2, 2, None, 1.0,
+                                 DUMMY, None, None) == 5
+    assert so.sparse_mla_combine(DUMMY, DUMMY, 0, 128, 2, 2, None, 1.0, None,
+                                 None, None) == 0
+
+
+def test_get_device_error_rejects_null(so):
+    assert so.sparse_mla_get_device_error(None, None, None, None, None) == 1
