@@ -1,0 +1,253 @@
+"""Benchmark: sparse MLA decode throughput on one MI355X.
+
+Workload (the per-token shape the headline metric is quoted on): H=128
+heads, table width / topk 2048 (128 SWA + 1920 compressed rows), BF16 q and
+KV rows, 128k context at compress ratio 4 (32768 compressed rows per
+request), per-head sinks, one token per request, decode batch T=512.  Inputs
+are seeded synthetic tensors (sparse_mla_decode_gather_amd.workloads),
+resident in HBM before timing starts.
+
+A step is one sparse_mla_decode call (planner + split kernel [+ combine]).
+Each launch is bracketed by HIP events on the stream it runs on, so the
+average launch duration, gathered bytes and FLOPs give the roofline numbers.
+
+Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
+--no-cpu-baseline, --sweep (adds per-T numbers for T in 1,4,8,64,256).
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
+ROW_BYTES = 1024                # one BF16 row of 512 elements
+COUNTERS = os.path.join(ROOT, "profiles", "decode_long_context_T512_counters.txt")
+
+
+def active_slots_per_token(w):
+    import torch
+    K = w.K
+    col = torch.arange(K, device=w.indices.device)[None, :]
+    lens = w.topk_lens[:, None] if w.topk_lens is not None else K
+    act = (col < lens) & (w.indices != -1)
+    return act.sum(1).cpu()
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "api.cpp", "internal.h"):
+        with open(os.path.join(ROOT, "sparse_mla_decode_gather_amd", "csrc", f),
+                  "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    vals = {}
+    with open(COUNTERS) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_launches(fn, steps, warmup, stream):
+    """Run fn() warmup+steps times; HIP events around each timed launch on
+    ``stream``.  Returns (total ms over the timed region, per-launch ms)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
+        enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in evs]
+    return start.elapsed_time(end), per
+
+
+def cpu_baseline(w, budget_s=12.0, max_tokens=512):
+    """The oracle (NumPy fp64, as it stands) on a bounded sample of the same
+    workload: the first n tokens, n chosen so the run takes ~budget_s."""
+    import numpy as np
+    import torch
+    import oracle
+    from sparse_mla_decode_gather_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()
+                     if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+
+    def host(tokens):
+        tok = torch.as_tensor(tokens, dtype=torch.long)
+        idx = w.indices.cpu()[tok].numpy().astype(np.int64)
+        out_idx = idx.copy()
+        pools = []
+        for sl, pool in ((slice(0, 128), w.swa_pool), (slice(128, None), w.comp_pool)):
+            part = idx[:, sl]
+            ok = part >= 0
+            uniq = np.unique(part[ok])
+            pools.append(W.raw_bits(pool[torch.as_tensor(uniq, device=pool.device)]))
+            rem = part.copy()
+            rem[ok] = np.searchsorted(uniq, part[ok])
+            out_idx[:, sl] = rem
+        return dict(q_bits=W.raw_bits(w.q[tok.to(w.q.device)]), q_dtype=w.q_dtype,
+                    swa_bits=pools[0], comp_bits=pools[1], kv_dtype=w.kv_dtype,
+                    indices=out_idx.astype(np.int32),
+                    topk_lens=w.topk_lens.cpu()[tok].numpy(),
+                    sinks=w.sinks.cpu().numpy())
+
+    def run(tokens):
+        case = host(tokens)            # input marshalling, not timed
+        t0 = time.perf_counter()
+        oracle.sparse_mla_decode(bmm1_scale=w.bmm1_scale,
+                                 bmm2_scale=w.bmm2_scale,
+                                 lse_scale=w.lse_scale, **case)
+        return time.perf_counter() - t0
+
+    one = run([0])
+    n = int(max(1, min(max_tokens, budget_s / max(one, 1e-3))))
+    secs = run(list(range(n)))
+    return {"value": round(n / secs, 3), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"first {n} of {w.T} tokens of the same workload "
+                      f"(NumPy float64 oracle, {secs:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not "
+              "supported (the sharding design is described in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mla_decode_gather_amd import lib, workloads as W
+
+    lib.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    w = W.make_long_context(args.T, "cuda", seed=4000 + args.T)
+    n_act = active_slots_per_token(w)
+    T = w.T
+    out = torch.empty((T, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    plan = lib.plan_splits(T, w.H, w.K)
+    ws = lib.alloc_workspace(plan, T, w.H)
+
+    def step():
+        lib.decode(w.q, w.swa_pool, w.comp_pool, w.indices, out, out_lse=lse,
+                   topk_lens=w.topk_lens, seq_lens=w.seq_lens, sinks=w.sinks,
+                   bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                   lse_scale=w.lse_scale, plan=plan, workspace=ws, stream=stream)
+
+    total_ms, per = time_launches(step, args.steps, args.warmup, stream)
+    ms_step = total_ms / args.steps
+    avg_launch_ms = sum(per) / len(per)
+    gathered = int(n_act.sum()) * ROW_BYTES
+    flops = 4.0 * 512 * w.H * int(n_act.sum())
+    achieved_gbps = gathered / (avg_launch_ms * 1e-3) / 1e9
+    achieved_tflops = flops / (avg_launch_ms * 1e-3) / 1e12
+    hbm_frac = achieved_gbps / HBM_PEAK_GBPS
+    mfma_frac = achieved_tflops / MFMA_BF16_PEAK_TFLOPS
+    # roofline time = max(bytes / HBM peak, flops / MFMA peak)
+    t_roof = max(gathered / (HBM_PEAK_GBPS * 1e9), flops / (MFMA_BF16_PEAK_TFLOPS * 1e12))
+    bound = "hbm" if gathered / HBM_PEAK_GBPS >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e3) else "mfma"
+    roofline = {
+        "bound": bound,
+        "achieved": round(achieved_gbps if bound == "hbm" else achieved_tflops, 1),
+        "peak": HBM_PEAK_GBPS if bound == "hbm" else MFMA_BF16_PEAK_TFLOPS,
+        "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
+        "frac": round(t_roof / (avg_launch_ms * 1e-3), 4),
+        "traffic": measured_traffic(),
+    }
+    result = {
+        "metric": "decode tokens/s + gathered-KV GB/s, H=128 topk=2048 bf16; "
+                  "% of roofline",
+        "value": round(T * args.steps / (total_ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"long-context decode batch: T={T} tokens (one per "
+                               "request), H=128, topk=2048 (128 SWA + 1920 "
+                               "compressed), BF16 q/KV, seq_len 131072, "
+                               "compress ratio 4, sinks",
+                   "T": T, "H": w.H, "K": w.K, "global_batch": T,
+                   "parallelism": "single GPU"},
+        "gathered_GBps": round(achieved_gbps, 1),
+        "gathered_bytes_per_step": gathered,
+        "tflops": round(achieved_tflops, 1),
+        "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
+        "avg_launch_ms": round(avg_launch_ms, 4),
+        "plan": plan.as_dict(),
+        "roofline": roofline,
+    }
+    if args.sweep:
+        sweep = {}
+        for t in (1, 4, 8, 64, 256):
+            if t > T:
+                continue
+            p = lib.plan_splits(t, w.H, w.K)
+            wsp = lib.alloc_workspace(p, t, w.H)
+            o2, l2 = out[:t], lse[:t]
+
+            def st(t=t, p=p, wsp=wsp, o2=o2, l2=l2):
+                lib.decode(w.q[:t], w.swa_pool, w.comp_pool, w.indices[:t], o2,
+                           out_lse=l2, topk_lens=w.topk_lens[:t], sinks=w.sinks,
+                           bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                           plan=p, workspace=wsp, stream=stream)
+            tot, pl = time_launches(st, 50, 5, stream)
+            g = int(n_act[:t].sum()) * ROW_BYTES
+            avg = sum(pl) / len(pl)
+            sweep[str(t)] = {"tokens_per_s": round(t * 50 / (tot * 1e-3), 1),
+                             "avg_launch_us": round(avg * 1e3, 2),
+                             "gathered_GBps": round(g / (avg * 1e-3) / 1e9, 1),
+                             "num_splits": p.num_splits,
+                             "roofline_frac": round(g / (HBM_PEAK_GBPS * 1e9) /
+                                                    (avg * 1e-3), 4)}
+        result["sweep"] = sweep
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,20 +44,23 @@ namespace {
 
 constexpr int kD = kHeadDim;
 constexpr int kTile = 32;          // rows per LDS tile
-constexpr int kThreads = 256;      // 4 wave64
 constexpr int kSeg = 2048;         // table columns compacted per pass
 constexpr int kRowBytes = kD * 2;  // a BF16 row
-// LDS row pitch: a BF16 row plus 16 B of padding.  Consecutive rows then
-// start 4 banks apart, so 16 lanes reading the same 16-B chunk of 16
-// consecutive rows hit distinct banks, and every LDS address of the kernel
-// is a per-lane base plus a compile-time immediate.
-constexpr int kRowPitch = kRowBytes + 16;
+// LDS row pitch: a BF16 row plus 48 B of padding (pitch = 48 mod 256).
+// 16 lanes reading the same 16-B chunk of 16 consecutive rows then hit 16
+// distinct 16-B bank groups, the 16 lanes of a transposed read (4 rows x 4
+// 8-byte columns) hit disjoint banks, and every LDS address of the kernel is
+// a per-lane base plus a compile-time immediate.
+constexpr int kRowPitch = kRowBytes + 48;
 constexpr int kTileBytes = kTile * kRowPitch;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleThreshold = 8.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -118,16 +121,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Byte offset of element 0 of 16-B chunk `chunk` (0..63) of tile row `row`.
-__device__ __forceinline__ int tile_off(int row, int chunk) {
-  return row * kRowPitch + (chunk << 4);
+// Wait until at most N vector-memory loads of this wave are outstanding
+// (they complete in issue order).  Only vmcnt is constrained.
+// Scheduling pattern for a fully unrolled run of NMFMA MFMAs that each
+// consume RD LDS reads: issue LEAD reads up front, then alternate one MFMA
+// with the reads of a later MFMA, then drain.  Bounds the number of operand
+// registers in flight.
+template <int LEAD, int RD, int NMFMA>
+__device__ __forceinline__ void sched_interleave() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);      // DS reads
+#pragma unroll
+  for (int i = 0; i < NMFMA - LEAD / RD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);      // DS reads
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, LEAD / RD, 0);
 }
 
-// Row of k-slot (g, j) of a 32-row tile in the PV operands: slot j < 4 is
-// row 4g+j of the first 16-row block, j >= 4 row 4g+j-4 of the second, the
-// order in which the S^T accumulators hold them.
-__device__ __forceinline__ int pv_row(int g, int j) {
-  return (j < 4) ? (g * 4 + j) : (16 + g * 4 + (j - 4));
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// One LDS-DMA row load: every lane fetches 16 bytes at `gaddr` and the
+// hardware stores lane i's bytes at LDS byte address lds_addr + 16 i.  Issued
+// from inline asm so that the compiler does not treat it as an LDS store it
+// must wait for before every later LDS read (the pipeline below orders the
+// tiles with explicit vmcnt waits and barriers).  M0 carries the LDS base;
+// it is saved and restored around the load, which samples it at issue.
+__device__ __forceinline__ void lds_dma_row16(const void* gaddr,
+                                              uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gaddr), "s"(lds_addr)
+      : "memory");
 }
 
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
@@ -142,18 +176,40 @@ __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
 // split kernel
 // ---------------------------------------------------------------------------
 
-template <int HB, bool Q_FP8, bool KV_FP8, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 1)
+// A 32x32x16 BF16 MFMA tile, as the hardware lays it out on a wave64:
+//   A (32 x 16): lane l holds A[l % 32][8*(l/32) .. +8)
+//   B (16 x 32): lane l holds B[8*(l/32) .. +8)[l % 32]
+//   C (32 x 32): lane l, register i holds C[8*(i/4) + 4*(l/32) + i%4][l % 32]
+// S^T = K Q^T puts tile rows on M and heads on N, so lane l owns head
+// l % 32 and the rows 8a + 4*(l/32) + b (a, b in 0..3) of a 32-row tile.
+// Read as the B operand of O^T = V^T P^T (K = rows), registers 8h .. 8h+7
+// of that accumulator are exactly the k-slots of the h-th 16-row MFMA step
+// when slot s of k-group kg stands for tile row 16h + 8*(s/4) + 4*kg + s%4.
+// V^T is fetched in that row order with ds_read_b64_tr_b16, which hands
+// output lane j of each 16-lane group element j%4 of the 8-byte words
+// addressed by input lanes 4e + j/4 (e = 0..3).
+
+__device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
+  return 8 * (i >> 2) + 4 * kg + (i & 3);
+}
+
+template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT>
+__global__ __launch_bounds__(NW * 64, 1)
 void decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[2][kTileBytes];
+  constexpr int H = NW * 32;              // one wave per 32 heads
+  constexpr int NT = NW * 64;
+  constexpr int RPW = kTile / NW;         // tile rows each wave gathers
+  // LDS-DMA gather keeps NSTAGE-1 tiles in flight; FP8 rows go through
+  // registers (widened to BF16) with one tile of prefetch.
+  constexpr int NSTAGE = KV_FP8 ? 2 : (NW == 4 ? 4 : 2);
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
   __shared__ int32_t slots[kSeg];
-  __shared__ int32_t wave_cnt[4];
+  __shared__ int32_t wave_cnt[NW];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;       // 16-lane group: k-group of MFMA operands
-  const int li = lane & 15;      // row / column inside a 16x16 block
-  constexpr int H = 64 * HB;
+  const int l32 = lane & 31;
+  const int kg = lane >> 5;
 
   // XCD-aware mapping: the hardware hands consecutive workgroup ids to the
   // 8 XCDs round-robin, so give each XCD a contiguous range of work items;
@@ -165,8 +221,7 @@ void decode_kernel(DecodeParams p) {
   const int item = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
   const int t = item / p.S;
   const int s = item - t * p.S;
-
-  const int head0 = wave * 16 * HB;
+  const int head = wave * 32 + l32;
 
   int len = p.topk_lens ? p.topk_lens[t] : p.K;
   if (p.validate && threadIdx.x == 0 && s == 0 && (len < 0 || len > p.K))
@@ -175,44 +230,47 @@ void decode_kernel(DecodeParams p) {
   const int c_begin = s * p.split_cols;
   const int c_end = min(len, c_begin + p.split_cols);
 
-  // ---- Q fragments (B operand of S^T = K Q^T): lane holds head li and
-  // dims [kk*32 + 8g, +8) for every 32-dim step kk.
-  bf16x8 qf[HB][16];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const int head = head0 + hb * 16 + li;
+  // Q^T fragments (B operand of S^T = K Q^T): lane holds head `head`,
+  // dims [16kk + 8kg, +8) for each 16-dim step kk.
+  bf16x8 qf[32];
+  {
     const size_t qrow = ((size_t)t * H + head) * kD;
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const int d0 = kk * 32 + g * 8;
+    for (int kk = 0; kk < 32; ++kk) {
+      const int d0 = kk * 16 + kg * 8;
       u32x4 v;
-      if constexpr (Q_FP8) {
-        const u32x2 raw = *(const u32x2*)((const uint8_t*)p.q + qrow + d0);
-        v = widen_e4m3fn_x8(raw);
-      } else {
+      if constexpr (Q_FP8)
+        v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
+      else
         v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
-      }
-      qf[hb][kk] = __builtin_bit_cast(bf16x8, v);
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // Drain the Q loads here: otherwise their waits land inside the tile
+  // loop, where vmcnt also counts the row gathers in flight.
+  wait_vmcnt<0>();
 
-  float m_run[HB], l_run[HB];
-  f32x4 o[32][HB];
+  float m_run = -INFINITY;   // reference max (base-2 logits) of head `head`
+  float l_run = 0.f;         // this lane's share of the normaliser
+  f32x16 o[16];              // O^T: d-block db, d = 32db + 8(i/4) + 4kg + i%4
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    m_run[hb] = -INFINITY;
-    l_run[hb] = 0.f;
+  for (int db = 0; db < 16; ++db)
 #pragma unroll
-    for (int db = 0; db < 32; ++db) o[db][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+  // per-lane LDS offsets inside a tile
+  const int qk_off = l32 * kRowPitch + kg * 16;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int tr_off = (4 * (grp >> 1) + (i16 >> 2)) * kRowPitch +
+                     (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 
   for (int seg0 = c_begin; seg0 < c_end; seg0 += kSeg) {
     const int seg1 = min(c_end, seg0 + kSeg);
 
     // ---- compact the active slots of this segment into LDS ----------------
-    __syncthreads();   // the previous segment's tiles no longer read slots[]
+    __syncthreads();   // the previous segment no longer reads slots[] / tiles
     int n_act = 0;
-    for (int c0 = seg0; c0 < seg1; c0 += kThreads) {
+    for (int c0 = seg0; c0 < seg1; c0 += NT) {
       const int c = c0 + threadIdx.x;
       bool act = false;
       int code = 0;
@@ -235,7 +293,7 @@ void decode_kernel(DecodeParams p) {
       __syncthreads();
       int off = n_act, tot = 0;
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
+      for (int w2 = 0; w2 < NW; ++w2) {
         const int cw = wave_cnt[w2];
         off += (w2 < wave) ? cw : 0;
         tot += cw;
@@ -244,189 +302,168 @@ void decode_kernel(DecodeParams p) {
       n_act += tot;
       __syncthreads();
     }
-
-    // ---- gather + attend, 32 rows per tile ---------------------------------
     const int ntiles = (n_act + kTile - 1) / kTile;
-    // Each wave stages 8 rows of a tile; lane `lane` carries 16-B chunk
-    // `lane` of a BF16 row (8 bytes of an FP8 row, widened before LDS).
-    u32x4 st16[8];
-    u32x2 st8[8];
 
-    auto load_tile = [&](int tile) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int si = tile * kTile + wave * 8 + jj;
-        if (si < n_act) {
-          const int code = slots[si];
-          const uint8_t* base = code < 0 ? p.comp : p.swa;
-          const int64_t row = (int64_t)(code & 0x7FFFFFFF);
-          const uint8_t* src = base + row * p.row_stride_bytes;
-          if constexpr (KV_FP8) st8[jj] = *(const u32x2*)(src + lane * 8);
-          else st16[jj] = *(const u32x4*)(src + lane * 16);
-        } else {
-          if constexpr (KV_FP8) st8[jj] = u32x2{0u, 0u};
-          else st16[jj] = u32x4{0u, 0u, 0u, 0u};
-        }
-      }
-    };
-    auto store_tile = [&](int buf) {
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = wave * 8 + jj;
-        u32x4 v;
-        if constexpr (KV_FP8) v = widen_e4m3fn_x8(st8[jj]);
-        else v = st16[jj];
-        *(u32x4*)(&kv_lds[buf][tile_off(j, lane)]) = v;
-      }
+    // Row j of a tile is slot tile*32 + j; the ragged tail of the last tile
+    // repeats the last active row (its logits are masked, so it adds 0).
+    auto row_src = [&](int tile, int j) -> const uint8_t* {
+      const int si = min(tile * kTile + j, n_act - 1);
+      const int code = slots[si];
+      const uint8_t* base = code < 0 ? p.comp : p.swa;
+      return base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
     };
 
-    if (ntiles > 0) {
-      load_tile(0);
-      store_tile(0);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < ntiles; ++it) {
-      const int buf = it & 1;
-      if (it + 1 < ntiles) load_tile(it + 1);    // in flight during compute
-      const uint8_t* tb = kv_lds[buf];
-      const int n_tile = min(kTile, n_act - it * kTile);
-
-      // S^T[row, head] for 2 row blocks x HB head blocks
-      f32x4 sacc[2][HB];
+    // ---- one 32-row tile: S^T, online softmax, O^T ------------------------
+    auto attend = [&](const uint8_t* tb, int n_tile) {
+      f32x16 sacc;
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) sacc[rb][hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 32; ++kk) {
+        const bf16x8 a = *(const bf16x8*)(tb + qk_off + kk * 32);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
+      }
+      // keep the row reads a few MFMAs ahead instead of hoisting all 32
+      sched_interleave<4, 1, 32>();
+      float x[16];
+      float tmax = -INFINITY;
 #pragma unroll
-      for (int kk = 0; kk < 16; ++kk) {
+      for (int i = 0; i < 16; ++i) {
+        x[i] = (tile_row_of_reg(i, kg) < n_tile) ? sacc[i] * p.scale_log2 : -INFINITY;
+        tmax = fmaxf(tmax, x[i]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const bool need = tmax > m_run + kRescaleThreshold;
+      if (__ballot(need) != 0ull) {
+        const float alpha = need ? fast_exp2(m_run - tmax) : 1.f;
+        if (need) m_run = tmax;
+        l_run *= alpha;
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-          const bf16x8 a = *(const bf16x8*)(tb + tile_off(rb * 16 + li, kk * 4 + g));
+        for (int db = 0; db < 16; ++db) o[db] *= alpha;
+      }
+      float lsum = 0.f;
+      bf16x8 pf[2];
 #pragma unroll
-          for (int hb = 0; hb < HB; ++hb)
-            sacc[rb][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, qf[hb][kk], sacc[rb][hb], 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        u32x4 pk;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float p0 = fast_exp2(x[8 * h + 2 * k] - m_run);
+          const float p1 = fast_exp2(x[8 * h + 2 * k + 1] - m_run);
+          lsum += p0 + p1;
+          pk[k] = pack_bf16x2(p0, p1);
+        }
+        pf[h] = __builtin_bit_cast(bf16x8, pk);
+      }
+      l_run += lsum;
+#pragma unroll
+      for (int db = 0; db < 16; ++db) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint8_t* vb = tb + tr_off + (16 * h) * kRowPitch + db * 64;
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4 __attribute__((address_space(3)))*)(vb));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+          const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, v), pf[h], o[db], 0, 0, 0);
         }
       }
+      sched_interleave<4, 2, 32>();
+    };
 
-      // online softmax (base 2) per head; lane holds head li, rows 4g+i of
-      // each row block
-      bf16x8 pf[HB];
-      float alpha[HB];
-      bool need_any = false;
-      float x[HB][8];
+    if constexpr (!KV_FP8) {
+      // LDS-DMA gather: one instruction moves one 1 KB row, lane i's 16 B
+      // landing at row base + 16 i.  Each wave gathers RPW rows per tile.
+      const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
+      auto issue = [&](int tile) {
+        const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = rb * 16 + g * 4 + i;
-            const float v = (row < n_tile) ? sacc[rb][hb][i] * p.scale_log2
-                                           : -INFINITY;
-            x[hb][rb * 4 + i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const bool need = tmax > m_run[hb] + kRescaleThreshold;
-        alpha[hb] = 1.f;
-        if (need) {
-          alpha[hb] = fast_exp2(m_run[hb] - tmax);
-          m_run[hb] = tmax;
+        for (int jj = 0; jj < RPW; ++jj) {
+          const int j = wave * RPW + jj;
+          lds_dma_row16(row_src(tile, j) + lane * 16,
+                        __builtin_amdgcn_readfirstlane(dst + j * kRowPitch));
         }
-        need_any |= need;
+      };
+      const int pro = min(NSTAGE - 1, ntiles);
+      for (int tl = 0; tl < pro; ++tl) issue(tl);
+      for (int it = 0; it < ntiles; ++it) {
+        // this wave's rows of tile `it` have landed once at most the rows
+        // of the tiles issued after it are still in flight
+        const int after = min(NSTAGE - 2, ntiles - 1 - it);
+        if (after >= 2) wait_vmcnt<2 * RPW>();
+        else if (after == 1) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();            // every wave's rows landed; tile it-1 done
+        if (it + NSTAGE - 1 < ntiles) issue(it + NSTAGE - 1);
+        attend(kv_lds + (it % NSTAGE) * kTileBytes, min(kTile, n_act - it * kTile));
       }
-      if (__ballot(need_any) != 0ull) {
+    } else {
+      // FP8 rows: 8 bytes per lane through registers, widened to BF16.
+      u32x2 st[RPW];
+      auto load = [&](int tile) {
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) {
-          l_run[hb] *= alpha[hb];
+        for (int jj = 0; jj < RPW; ++jj)
+          st[jj] = *(const u32x2*)(row_src(tile, wave * RPW + jj) + lane * 8);
+      };
+      auto store = [&](int tile) {
+        uint8_t* dst = kv_lds + (tile & 1) * kTileBytes;
 #pragma unroll
-          for (int db = 0; db < 32; ++db) o[db][hb] *= alpha[hb];
-        }
+        for (int jj = 0; jj < RPW; ++jj)
+          *(u32x4*)(dst + (wave * RPW + jj) * kRowPitch + lane * 16) =
+              widen_e4m3fn_x8(st[jj]);
+      };
+      if (ntiles > 0) {
+        load(0);
+        store(0);
       }
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        float pv[8];
-        float lsum = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = fast_exp2(x[hb][j] - m_run[hb]);
-          lsum += pv[j];
-        }
-        l_run[hb] += lsum;
-        u32x4 packed;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) packed[k] = pack_bf16x2(pv[2 * k], pv[2 * k + 1]);
-        pf[hb] = __builtin_bit_cast(bf16x8, packed);
+      for (int it = 0; it < ntiles; ++it) {
+        __syncthreads();            // tile it stored; tile it-1 done
+        if (it + 1 < ntiles) load(it + 1);
+        attend(kv_lds + (it & 1) * kTileBytes, min(kTile, n_act - it * kTile));
+        if (it + 1 < ntiles) store(it + 1);
       }
-
-      // O^T[d, head] += V^T[d, rows] * P^T[rows, head]
-#pragma unroll
-      for (int db = 0; db < 32; ++db) {
-        const int d = db * 16 + li;
-        const int chunk = d >> 3;
-        const int sub = (d & 7) * 2;
-        bf16x8 a;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = pv_row(g, j);
-          a[j] = *(const __bf16*)(tb + tile_off(row, chunk) + sub);
-        }
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
-          o[db][hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf[hb], o[db][hb],
-                                                              0, 0, 0);
-      }
-
-      if (it + 1 < ntiles) store_tile(buf ^ 1);
-      __syncthreads();
     }
   }
 
   // ---- epilogue ------------------------------------------------------------
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    float l = l_run[hb];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
-    float m = m_run[hb];
-    const int head = head0 + hb * 16 + li;
-    float inv, lse;
-    if constexpr (SPLIT) {
-      inv = (l > 0.f) ? p.bmm2 / l : 0.f;
-      lse = (l > 0.f) ? m + fast_log2(l) : -INFINITY;
-    } else {
-      float fac = 1.f;
-      if (p.sinks) {
-        const float sl = p.sinks[head] * kLog2e;
-        const float mm = fmaxf(m, sl);
-        fac = fast_exp2(m - mm);     // 0 when nothing was active (m = -inf)
-        l = l * fac + fast_exp2(sl - mm);
-        m = mm;
-      }
-      inv = (l > 0.f) ? fac * p.bmm2 / l : 0.f;
-      lse = (l > 0.f) ? p.lse_scale * (m + fast_log2(l)) : -INFINITY;
+  float l = l_run + __shfl_xor(l_run, 32);
+  float m = m_run;
+  float inv, lse;
+  if constexpr (SPLIT) {
+    inv = (l > 0.f) ? p.bmm2 / l : 0.f;
+    lse = (l > 0.f) ? m + fast_log2(l) : -INFINITY;
+  } else {
+    float fac = 1.f;
+    if (p.sinks) {
+      const float sl = p.sinks[head] * kLog2e;
+      const float mm = fmaxf(m, sl);
+      fac = fast_exp2(m - mm);       // 0 when nothing was active (m = -inf)
+      l = l * fac + fast_exp2(sl - mm);
+      m = mm;
     }
-    uint16_t* dst;
-    if constexpr (SPLIT)
-      dst = p.mid_out + (((size_t)t * H + head) * p.S + s) * kD;
-    else
-      dst = (uint16_t*)p.out + ((size_t)t * H + head) * kD;
+    inv = (l > 0.f) ? fac * p.bmm2 / l : 0.f;
+    lse = (l > 0.f) ? p.lse_scale * (m + fast_log2(l)) : -INFINITY;
+  }
+  uint16_t* dst;
+  if constexpr (SPLIT)
+    dst = p.mid_out + (((size_t)t * H + head) * p.S + s) * kD;
+  else
+    dst = (uint16_t*)p.out + ((size_t)t * H + head) * kD;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      const f32x4 v = o[db][hb];
+  for (int db = 0; db < 16; ++db) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
       u32x2 w;
-      w[0] = pack_bf16x2(v[0] * inv, v[1] * inv);
-      w[1] = pack_bf16x2(v[2] * inv, v[3] * inv);
-      *(u32x2*)(dst + db * 16 + g * 4) = w;
+      w[0] = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
+      w[1] = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
+      *(u32x2*)(dst + db * 32 + a * 8 + kg * 4) = w;
     }
-    if (g == 0) {
-      if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
-      else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
-    }
+  }
+  if (kg == 0) {
+    if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
+    else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
   }
 }
 
@@ -477,14 +514,14 @@ __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
 
-template <int HB, bool QF, bool KF>
+template <int NW, bool QF, bool KF>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   if (p.S > 1)
-    hipLaunchKernelGGL((decode_kernel<HB, QF, KF, true>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true>), grid, dim3(NW * 64), 0,
                        stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<HB, QF, KF, false>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false>), grid, dim3(NW * 64), 0,
                        stream, p);
   return hipGetLastError();
 }
@@ -495,13 +532,13 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream) {
   const bool qf = q_dtype != 0, kf = kv_dtype != 0;
   if (p.H == 64) {
-    if (!qf && !kf) return launch_decode_t<1, false, false>(p, stream);
-    if (qf && kf) return launch_decode_t<1, true, true>(p, stream);
-    return launch_decode_t<1, false, true>(p, stream);
+    if (!qf && !kf) return launch_decode_t<2, false, false>(p, stream);
+    if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
+    return launch_decode_t<2, false, true>(p, stream);
   }
-  if (!qf && !kf) return launch_decode_t<2, false, false>(p, stream);
-  if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
-  return launch_decode_t<2, false, true>(p, stream);
+  if (!qf && !kf) return launch_decode_t<4, false, false>(p, stream);
+  if (qf && kf) return launch_decode_t<4, true, true>(p, stream);
+  return launch_decode_t<4, false, true>(p, stream);
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
