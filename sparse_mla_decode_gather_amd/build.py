@@ -23,10 +23,7 @@ ARCH = "gfx950"
 SOURCES = ["kernels.hip", "api.cpp"]
 
 # Packed FP32 VALU forms are kept out of the generated code on purpose.
-# MFMA results go to VGPRs (the AGPR file then holds what does not fit):
-# with the default heuristic the decode kernel spills to scratch.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
 def hipcc() -> str:

@@ -54,7 +54,10 @@ constexpr int kRowBytes = kD * 2;  // a BF16 row
 constexpr int kRowPitch = kRowBytes + 48;
 constexpr int kTileBytes = kTile * kRowPitch;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleThreshold = 8.0f;
+// A tile may exceed the running reference max by this much (base-2 logit
+// units) before the split is restarted with a higher reference: with
+// p <= 2^64 every probability and partial sum stays finite in BF16/FP32.
+constexpr float kRefSlack = 64.0f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -94,11 +97,14 @@ __device__ __forceinline__ u32x4 widen_e4m3fn_x8(u32x2 v) {
   return r;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats -> two BF16 (round to nearest even) packed in one dword
+// (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo;   // round to nearest even
-  __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) {
@@ -123,6 +129,30 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Wait until at most N vector-memory loads of this wave are outstanding
 // (they complete in issue order).  Only vmcnt is constrained.
+// S^T = K Q^T is issued from inline asm so that its 16-register accumulator
+// lives in VGPRs while the compiler keeps the O^T accumulators (the PV
+// builtin) in AGPRs: both products as builtins would need 272 accumulator
+// registers of one kind.  The asm follows the MFMA hazard rules the
+// compiler itself applies on gfx950: an MFMA may accumulate into the result
+// of the previous MFMA of the same opcode back to back; an operand written
+// by a VALU instruction needs 2 wait states before an MFMA reads it; a VALU
+// read of an MFMA result needs the MFMA's passes plus a few wait states (18
+// are inserted, more than the compiler's own 11).  The statements are not
+// volatile, so LDS reads can still be scheduled ahead of them; their order
+// follows the data dependence through the accumulator.
+__device__ __forceinline__ f32x16 mfma_qk_first(bf16x8 a, bf16x8 b) {
+  f32x16 d;
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+      : "=&v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, bf16x8 a, bf16x8 b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk_drain(f32x16& acc) {
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(acc));
+}
+
 // Scheduling pattern for a fully unrolled run of NMFMA MFMAs that each
 // consume RD LDS reads: issue LEAD reads up front, then alternate one MFMA
 // with the reads of a later MFMA, then drain.  Bounds the number of operand
@@ -150,17 +180,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // must wait for before every later LDS read (the pipeline below orders the
 // tiles with explicit vmcnt waits and barriers).  M0 carries the LDS base;
 // it is saved and restored around the load, which samples it at issue.
-__device__ __forceinline__ void lds_dma_row16(const void* gaddr,
+//
+// The row address is wave-uniform: it lives in SGPRs (`row`) and each lane
+// adds its own byte offset `lane_off` (16 * lane), so issuing a row costs
+// scalar work only.
+__device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
+                                              uint32_t lane_off,
                                               uint32_t lds_addr) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(gaddr), "s"(lds_addr)
+      : "v"(lane_off), "s"(row), "s"(lds_addr)
       : "memory");
 }
 
@@ -205,9 +240,11 @@ void decode_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
   __shared__ int32_t slots[kSeg];
   __shared__ int32_t wave_cnt[NW];
+  __shared__ int32_t restart_flag;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // in an SGPR
   const int l32 = lane & 31;
   const int kg = lane >> 5;
 
@@ -264,7 +301,11 @@ void decode_kernel(DecodeParams p) {
   const int tr_off = (4 * (grp >> 1) + (i16 >> 2)) * kRowPitch +
                      (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 
-  for (int seg0 = c_begin; seg0 < c_end; seg0 += kSeg) {
+  if (threadIdx.x == 0) restart_flag = 0;
+  bool again;
+  do {
+  again = false;
+  for (int seg0 = c_begin; seg0 < c_end && !again; seg0 += kSeg) {
     const int seg1 = min(c_end, seg0 + kSeg);
 
     // ---- compact the active slots of this segment into LDS ----------------
@@ -306,41 +347,40 @@ void decode_kernel(DecodeParams p) {
 
     // Row j of a tile is slot tile*32 + j; the ragged tail of the last tile
     // repeats the last active row (its logits are masked, so it adds 0).
+    // (`tile` and `j` are wave-uniform, so the slot code is read into an
+    // SGPR and the address is computed on the scalar unit.)
     auto row_src = [&](int tile, int j) -> const uint8_t* {
       const int si = min(tile * kTile + j, n_act - 1);
-      const int code = slots[si];
+      const int code = __builtin_amdgcn_readfirstlane(slots[si]);
       const uint8_t* base = code < 0 ? p.comp : p.swa;
       return base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
     };
 
     // ---- one 32-row tile: S^T, online softmax, O^T ------------------------
     auto attend = [&](const uint8_t* tb, int n_tile) {
-      f32x16 sacc;
+      f32x16 sacc = mfma_qk_first(*(const bf16x8*)(tb + qk_off), qf[0]);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      for (int kk = 1; kk < 32; ++kk)
+        mfma_qk(sacc, *(const bf16x8*)(tb + qk_off + kk * 32), qf[kk]);
+      mfma_qk_drain(sacc);
+      // Rows past n_tile (ragged last tile) repeat the tile's last active
+      // row, so they cannot raise the max; their probabilities are zeroed
+      // below.
+      float smax = sacc[0];
 #pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const bf16x8 a = *(const bf16x8*)(tb + qk_off + kk * 32);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], sacc, 0, 0, 0);
-      }
-      // keep the row reads a few MFMAs ahead instead of hoisting all 32
-      sched_interleave<4, 1, 32>();
-      float x[16];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        x[i] = (tile_row_of_reg(i, kg) < n_tile) ? sacc[i] * p.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, x[i]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const bool need = tmax > m_run + kRescaleThreshold;
-      if (__ballot(need) != 0ull) {
-        const float alpha = need ? fast_exp2(m_run - tmax) : 1.f;
-        if (need) m_run = tmax;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < 16; ++db) o[db] *= alpha;
-      }
+      for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sacc[i]);
+      smax = fmaxf(smax, __shfl_xor(smax, 32));
+      const float tmax = smax * p.scale_log2;       // scale_log2 > 0
+      // The reference max is set by the first tile and then left alone
+      // (O is never rescaled in this loop).  A tile that outgrows it by
+      // more than kRefSlack asks for a restart with its max as reference;
+      // its own (possibly overflowing) contribution is discarded then.
+      if (m_run == -INFINITY) m_run = tmax;
+      const bool need = tmax > m_run + kRefSlack;
+      if (need) m_run = tmax;
+      if (__ballot(need) != 0ull && lane == 0) restart_flag = 1;
+      // p = 2^(s * scale_log2 - m_run)
+      const float neg_m = -m_run;
       float lsum = 0.f;
       bf16x8 pf[2];
 #pragma unroll
@@ -348,8 +388,10 @@ void decode_kernel(DecodeParams p) {
         u32x4 pk;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const float p0 = fast_exp2(x[8 * h + 2 * k] - m_run);
-          const float p1 = fast_exp2(x[8 * h + 2 * k + 1] - m_run);
+          float p0 = fast_exp2(__builtin_fmaf(sacc[8 * h + 2 * k], p.scale_log2, neg_m));
+          float p1 = fast_exp2(__builtin_fmaf(sacc[8 * h + 2 * k + 1], p.scale_log2, neg_m));
+          if (tile_row_of_reg(8 * h + 2 * k, kg) >= n_tile) p0 = 0.f;
+          if (tile_row_of_reg(8 * h + 2 * k + 1, kg) >= n_tile) p1 = 0.f;
           lsum += p0 + p1;
           pk[k] = pack_bf16x2(p0, p1);
         }
@@ -357,9 +399,9 @@ void decode_kernel(DecodeParams p) {
       }
       l_run += lsum;
 #pragma unroll
-      for (int db = 0; db < 16; ++db) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int db = 0; db < 16; ++db) {
           const uint8_t* vb = tb + tr_off + (16 * h) * kRowPitch + db * 64;
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
               (s16x4 __attribute__((address_space(3)))*)(vb));
@@ -370,20 +412,20 @@ void decode_kernel(DecodeParams p) {
               __builtin_bit_cast(bf16x8, v), pf[h], o[db], 0, 0, 0);
         }
       }
-      sched_interleave<4, 2, 32>();
+      sched_interleave<8, 2, 32>();
     };
 
     if constexpr (!KV_FP8) {
       // LDS-DMA gather: one instruction moves one 1 KB row, lane i's 16 B
       // landing at row base + 16 i.  Each wave gathers RPW rows per tile.
       const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
+      const uint32_t lane_off = (uint32_t)lane * 16u;
       auto issue = [&](int tile) {
         const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
 #pragma unroll
         for (int jj = 0; jj < RPW; ++jj) {
-          const int j = wave * RPW + jj;
-          lds_dma_row16(row_src(tile, j) + lane * 16,
-                        __builtin_amdgcn_readfirstlane(dst + j * kRowPitch));
+          const int j = wave_u * RPW + jj;
+          lds_dma_row16(row_src(tile, j), lane_off, dst + j * kRowPitch);
         }
       };
       const int pro = min(NSTAGE - 1, ntiles);
@@ -396,6 +438,10 @@ void decode_kernel(DecodeParams p) {
         else if (after == 1) wait_vmcnt<RPW>();
         else wait_vmcnt<0>();
         __syncthreads();            // every wave's rows landed; tile it-1 done
+        if (restart_flag) {
+          again = true;
+          break;
+        }
         if (it + NSTAGE - 1 < ntiles) issue(it + NSTAGE - 1);
         attend(kv_lds + (it % NSTAGE) * kTileBytes, min(kTile, n_act - it * kTile));
       }
@@ -405,7 +451,7 @@ void decode_kernel(DecodeParams p) {
       auto load = [&](int tile) {
 #pragma unroll
         for (int jj = 0; jj < RPW; ++jj)
-          st[jj] = *(const u32x2*)(row_src(tile, wave * RPW + jj) + lane * 8);
+          st[jj] = *(const u32x2*)(row_src(tile, wave_u * RPW + jj) + lane * 8);
       };
       auto store = [&](int tile) {
         uint8_t* dst = kv_lds + (tile & 1) * kTileBytes;
@@ -420,12 +466,31 @@ void decode_kernel(DecodeParams p) {
       }
       for (int it = 0; it < ntiles; ++it) {
         __syncthreads();            // tile it stored; tile it-1 done
+        if (restart_flag) {
+          again = true;
+          break;
+        }
         if (it + 1 < ntiles) load(it + 1);
         attend(kv_lds + (it & 1) * kTileBytes, min(kTile, n_act - it * kTile));
         if (it + 1 < ntiles) store(it + 1);
       }
     }
+    // a restart asked for by the segment's last tile
+    __syncthreads();
+    if (restart_flag) again = true;
   }
+  if (again) {
+    // Rare: start the split over with the raised reference maxima.
+    wait_vmcnt<0>();                // no row gather may still be landing
+    __syncthreads();
+    if (threadIdx.x == 0) restart_flag = 0;
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+  }
+  } while (again);
 
   // ---- epilogue ------------------------------------------------------------
   float l = l_run + __shfl_xor(l_run, 32);

@@ -195,6 +195,40 @@ def test_topk_edges_ragged_tiles_and_masks():
         check(custom(idx, lens=lens, H=H, sinks=False), what=f"edges H={H} nosink")
 
 
+def test_large_logit_range_restarts_are_exact():
+    """Logits spread far wider than the 64 (base-2) slack the kernel allows
+    above its first-tile reference max, so later tiles force the split to
+    restart with a higher reference; the result must still match."""
+    need_gpu()
+    rng = np.random.default_rng(11)
+    idx = np.concatenate([rng.integers(0, 600, (4, 128)),
+                          rng.integers(0, 900, (4, 1400))], 1).astype(np.int32)
+    # scores ~ N(0, (2*sqrt(512))^2): std ~45 natural, ~65 in base 2
+    w = custom(idx, lens=[1528, 900, 200, 1528], b1=2.0)
+    check(w, what="wide logits unsplit", plan=L.plan_splits(4, 128, 1528, num_splits=1))
+    check(w, what="wide logits S=4", plan=L.plan_splits(4, 128, 1528, num_splits=4))
+
+
+def test_increasing_logits_force_repeated_restarts():
+    """Row i of the table is (i/40)*u for a fixed direction u and q = u, so
+    the logits rise by ~100 (base-2) every 32-row tile."""
+    need_gpu()
+    T, K, H = 2, 700, 64
+    u = torch.zeros(512)
+    u[:8] = 1.0
+    rows = torch.stack([u * (i / 40.0) for i in range(K)]).to(torch.bfloat16)
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    idx[:, :128] = np.arange(128)
+    w = W.Workload(name="rising", T=T, H=H, K=K,
+                   q=u.to(torch.bfloat16).expand(T, H, 512).contiguous().cuda(),
+                   q_dtype=W.BF16, swa_pool=rows.cuda(), comp_pool=rows.cuda(),
+                   kv_dtype=W.BF16, indices=torch.from_numpy(idx).cuda(),
+                   topk_lens=None,
+                   seq_lens=torch.full((T,), 4096, dtype=torch.int32, device="cuda"),
+                   cum_seq_lens_q=None, sinks=None, bmm1_scale=4.0, bmm2_scale=1.0)
+    check(w, what="rising logits")
+
+
 def test_duplicate_indices_count_per_slot():
     need_gpu()
     idx = np.zeros((3, 300), np.int32)
