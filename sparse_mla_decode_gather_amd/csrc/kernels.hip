@@ -115,6 +115,13 @@ __device__ __forceinline__ float fast_log2(float x) {
   return __builtin_amdgcn_logf(x);    // v_log_f32 (base 2)
 }
 
+// max(v[i], v[i ^ 32]) on every lane, with one VALU lane swap (no LDS).
+__device__ __forceinline__ float max_with_other_half(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v),
+                                                  __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -151,21 +158,6 @@ __device__ __forceinline__ void mfma_qk(f32x16& acc, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void mfma_qk_drain(f32x16& acc) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(acc));
-}
-
-// Scheduling pattern for a fully unrolled run of NMFMA MFMAs that each
-// consume RD LDS reads: issue LEAD reads up front, then alternate one MFMA
-// with the reads of a later MFMA, then drain.  Bounds the number of operand
-// registers in flight.
-template <int LEAD, int RD, int NMFMA>
-__device__ __forceinline__ void sched_interleave() {
-  __builtin_amdgcn_sched_group_barrier(0x100, LEAD, 0);      // DS reads
-#pragma unroll
-  for (int i = 0; i < NMFMA - LEAD / RD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);      // DS reads
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, LEAD / RD, 0);
 }
 
 template <int N>
@@ -234,11 +226,14 @@ void decode_kernel(DecodeParams p) {
   constexpr int H = NW * 32;              // one wave per 32 heads
   constexpr int NT = NW * 64;
   constexpr int RPW = kTile / NW;         // tile rows each wave gathers
-  // LDS-DMA gather keeps NSTAGE-1 tiles in flight; FP8 rows go through
-  // registers (widened to BF16) with one tile of prefetch.
+  // Row gather into NSTAGE LDS tiles.  BF16 rows use LDS-DMA loads, which
+  // need no registers (this kernel has none to spare); FP8 rows go through
+  // registers (8 bytes per lane) and are widened to BF16 on the way.  The
+  // loads for tile it+NSTAGE-1 are in flight while tile it is computed.
+  constexpr bool USE_DMA = !KV_FP8;
   constexpr int NSTAGE = KV_FP8 ? 2 : (NW == 4 ? 4 : 2);
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
-  __shared__ int32_t slots[kSeg];
+  __shared__ __attribute__((aligned(16))) int32_t slots[kSeg];
   __shared__ int32_t wave_cnt[NW];
   __shared__ int32_t restart_flag;
 
@@ -302,6 +297,101 @@ void decode_kernel(DecodeParams p) {
                      (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
 
   if (threadIdx.x == 0) restart_flag = 0;
+  // A per-lane sticky flag: some tile outgrew the reference max by more
+  // than kRefSlack (m_run has then been raised to that tile's max).  It is
+  // checked once per segment; tiles processed after it are discarded by the
+  // restart, and one restart always suffices since m_run only grows.
+  bool need_sticky = false;
+
+  // ---- the three phases of a 32-row tile ------------------------------------
+  // S^T for a tile (raw logits, before bmm1_scale).
+  // The MFMA operand reads run kLead steps ahead of the MFMAs; the order is
+  // pinned with scheduling barriers (the compiler then counts the LDS reads
+  // in flight and waits for exactly the one each MFMA needs).
+  constexpr int kLead = 4;
+  auto qk = [&](const uint8_t* tb, auto&& every4) -> f32x16 {
+    bf16x8 a[kLead];
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
+    f32x16 acc;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
+      else mfma_qk(acc, a[kk % kLead], qf[kk]);
+      if (kk + kLead < 32)
+        a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
+      if ((kk & 3) == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        every4(kk >> 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return acc;
+  };
+
+  // Online softmax of one tile's S^T; returns P^T as the two B operands of
+  // the PV steps.  Rows past n_tile (a ragged last tile) repeat the tile's
+  // last active row: they cannot raise the max and get probability 0.
+  auto softmax = [&](f32x16 sv, int n_tile, bf16x8 (&pf)[2]) {
+    mfma_qk_drain(sv);
+    float smax = sv[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+    smax = max_with_other_half(smax);
+    const float tmax = smax * p.scale_log2;       // scale_log2 > 0
+    // The reference max is set by the first tile and then left alone, so O
+    // is never rescaled inside the loop.
+    m_run = (m_run == -INFINITY) ? tmax : m_run;
+    const bool need = tmax > m_run + kRefSlack;
+    m_run = need ? tmax : m_run;
+    need_sticky |= need;
+    const float neg_m = -m_run;
+    float lsum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 pk;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i0 = 8 * h + 2 * k;
+        float p0 = fast_exp2(__builtin_fmaf(sv[i0], p.scale_log2, neg_m));
+        float p1 = fast_exp2(__builtin_fmaf(sv[i0 + 1], p.scale_log2, neg_m));
+        if (n_tile < kTile) {         // wave-uniform; only a ragged last tile
+          p0 = (tile_row_of_reg(i0, kg) < n_tile) ? p0 : 0.f;
+          p1 = (tile_row_of_reg(i0 + 1, kg) < n_tile) ? p1 : 0.f;
+        }
+        lsum += p0 + p1;
+        pk[k] = pack_bf16x2(p0, p1);
+      }
+      pf[h] = __builtin_bit_cast(bf16x8, pk);
+    }
+    l_run += lsum;
+  };
+  // O^T += V^T P^T for a tile: step k covers rows [16h, 16h+16) (h = k/16)
+  // of d-block db = k%16.
+  auto pv = [&](const uint8_t* tb, const bf16x8 (&pf)[2]) {
+    auto vfrag = [&](int k) -> bf16x8 {
+      const uint8_t* vb = tb + tr_off + (16 * (k >> 4)) * kRowPitch + (k & 15) * 64;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+      return __builtin_bit_cast(bf16x8,
+                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 v[kLead];
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) v[k] = vfrag(k);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k % kLead], pf[k >> 4],
+                                                         o[k & 15], 0, 0, 0);
+      if (k + kLead < 32) v[k % kLead] = vfrag(k + kLead);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   bool again;
   do {
   again = false;
@@ -344,146 +434,151 @@ void decode_kernel(DecodeParams p) {
       __syncthreads();
     }
     const int ntiles = (n_act + kTile - 1) / kTile;
+    auto n_in = [&](int tile) { return min(kTile, n_act - tile * kTile); };
 
     // Row j of a tile is slot tile*32 + j; the ragged tail of the last tile
-    // repeats the last active row (its logits are masked, so it adds 0).
-    // (`tile` and `j` are wave-uniform, so the slot code is read into an
-    // SGPR and the address is computed on the scalar unit.)
-    auto row_src = [&](int tile, int j) -> const uint8_t* {
-      const int si = min(tile * kTile + j, n_act - 1);
-      const int code = __builtin_amdgcn_readfirstlane(slots[si]);
-      const uint8_t* base = code < 0 ? p.comp : p.swa;
-      return base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+    // repeats the last active row.  Slot codes are wave-uniform: they are
+    // read into SGPRs and row addresses are computed on the scalar unit.
+    auto stage = [&](int tile) -> const uint8_t* {
+      return kv_lds + (tile % NSTAGE) * kTileBytes;
     };
 
-    // ---- one 32-row tile: S^T, online softmax, O^T ------------------------
-    auto attend = [&](const uint8_t* tb, int n_tile) {
-      f32x16 sacc = mfma_qk_first(*(const bf16x8*)(tb + qk_off), qf[0]);
-#pragma unroll
-      for (int kk = 1; kk < 32; ++kk)
-        mfma_qk(sacc, *(const bf16x8*)(tb + qk_off + kk * 32), qf[kk]);
-      mfma_qk_drain(sacc);
-      // Rows past n_tile (ragged last tile) repeat the tile's last active
-      // row, so they cannot raise the max; their probabilities are zeroed
-      // below.
-      float smax = sacc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sacc[i]);
-      smax = fmaxf(smax, __shfl_xor(smax, 32));
-      const float tmax = smax * p.scale_log2;       // scale_log2 > 0
-      // The reference max is set by the first tile and then left alone
-      // (O is never rescaled in this loop).  A tile that outgrows it by
-      // more than kRefSlack asks for a restart with its max as reference;
-      // its own (possibly overflowing) contribution is discarded then.
-      if (m_run == -INFINITY) m_run = tmax;
-      const bool need = tmax > m_run + kRefSlack;
-      if (need) m_run = tmax;
-      if (__ballot(need) != 0ull && lane == 0) restart_flag = 1;
-      // p = 2^(s * scale_log2 - m_run)
-      const float neg_m = -m_run;
-      float lsum = 0.f;
-      bf16x8 pf[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        u32x4 pk;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          float p0 = fast_exp2(__builtin_fmaf(sacc[8 * h + 2 * k], p.scale_log2, neg_m));
-          float p1 = fast_exp2(__builtin_fmaf(sacc[8 * h + 2 * k + 1], p.scale_log2, neg_m));
-          if (tile_row_of_reg(8 * h + 2 * k, kg) >= n_tile) p0 = 0.f;
-          if (tile_row_of_reg(8 * h + 2 * k + 1, kg) >= n_tile) p1 = 0.f;
-          lsum += p0 + p1;
-          pk[k] = pack_bf16x2(p0, p1);
-        }
-        pf[h] = __builtin_bit_cast(bf16x8, pk);
-      }
-      l_run += lsum;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int db = 0; db < 16; ++db) {
-          const uint8_t* vb = tb + tr_off + (16 * h) * kRowPitch + db * 64;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)(vb));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
-          const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, v), pf[h], o[db], 0, 0, 0);
-        }
-      }
-      sched_interleave<8, 2, 32>();
-    };
-
-    if constexpr (!KV_FP8) {
+    if constexpr (USE_DMA) {
       // LDS-DMA gather: one instruction moves one 1 KB row, lane i's 16 B
       // landing at row base + 16 i.  Each wave gathers RPW rows per tile.
       const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
       const uint32_t lane_off = (uint32_t)lane * 16u;
-      auto issue = [&](int tile) {
-        const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
+      // The wave's RPW slot codes of a tile are consecutive in slots[]:
+      // fetch them with wide LDS reads (one wait), then issue the rows.
+      // Reads past n_act stay inside slots[] (kSeg is a multiple of 32)
+      // and are replaced by the last active row.
+      const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
+      auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
+        const int s0 = tile * kTile + wave_u * RPW;
 #pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) {
-          const int j = wave_u * RPW + jj;
-          lds_dma_row16(row_src(tile, j), lane_off, dst + j * kRowPitch);
+        for (int q = 0; q < RPW / 4; ++q) {
+          const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
         }
+      };
+      auto issue_row = [&](int tile, int jj, const int (&codes)[RPW]) {
+        const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
+        const int s0 = tile * kTile + wave_u * RPW;
+        int code = __builtin_amdgcn_readfirstlane(codes[jj]);
+        code = (s0 + jj < n_act) ? code : last_code;
+        const uint8_t* base = code < 0 ? p.comp : p.swa;
+        const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+        lds_dma_row16(row, lane_off, dst + (wave_u * RPW + jj) * kRowPitch);
+      };
+      auto issue = [&](int tile) {
+        int codes[RPW];
+        fetch_codes(tile, codes);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) issue_row(tile, jj, codes);
+      };
+      // wait until this wave's rows of `tile` landed, given the last tile
+      // issued so far
+      auto wait_tile = [&](int tile, int last_issued) {
+        const int after = last_issued - tile;
+        if (after >= 2) wait_vmcnt<2 * RPW>();
+        else if (after == 1) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
       };
       const int pro = min(NSTAGE - 1, ntiles);
       for (int tl = 0; tl < pro; ++tl) issue(tl);
       for (int it = 0; it < ntiles; ++it) {
-        // this wave's rows of tile `it` have landed once at most the rows
-        // of the tiles issued after it are still in flight
-        const int after = min(NSTAGE - 2, ntiles - 1 - it);
-        if (after >= 2) wait_vmcnt<2 * RPW>();
-        else if (after == 1) wait_vmcnt<RPW>();
-        else wait_vmcnt<0>();
+        wait_tile(it, min(it + NSTAGE - 2, ntiles - 1));
         __syncthreads();            // every wave's rows landed; tile it-1 done
-        if (restart_flag) {
-          again = true;
-          break;
-        }
-        if (it + NSTAGE - 1 < ntiles) issue(it + NSTAGE - 1);
-        attend(kv_lds + (it % NSTAGE) * kTileBytes, min(kTile, n_act - it * kTile));
+        // The rows of tile it+NSTAGE-1 go out while the S^T MFMAs of tile
+        // it run (RPW rows, spread over the 32 MFMAs).
+        const int nxt = it + NSTAGE - 1;
+        const bool do_issue = nxt < ntiles;
+        int codes[RPW];
+        fetch_codes(do_issue ? nxt : it, codes);
+        const f32x16 sv = qk(stage(it), [&](int q) {
+          static_assert(RPW == 8 || RPW == 16, "rows per wave");
+#pragma unroll
+          for (int r = 0; r < RPW / 8; ++r)
+            if (do_issue) issue_row(nxt, q * (RPW / 8) + r, codes);
+        });
+        bf16x8 pf[2];
+        softmax(sv, n_in(it), pf);
+        pv(stage(it), pf);
       }
     } else {
-      // FP8 rows: 8 bytes per lane through registers, widened to BF16.
-      u32x2 st[RPW];
-      auto load = [&](int tile) {
+      // Register-staged gather: lane `lane` carries 16 B of a BF16 row (8 B
+      // of an FP8 row, widened to BF16 when written to LDS).  The loads of
+      // tile it+NSTAGE-1 are issued while the S^T MFMAs of tile it run and
+      // written to LDS after its O^T MFMAs, into the stage tile it-1 used.
+      constexpr int VW = KV_FP8 ? 2 : 4;          // dwords per lane per row
+      typedef uint32_t stage_t __attribute__((ext_vector_type(VW)));
+      const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
+      const uint32_t lane_off = (uint32_t)lane * (VW * 4);
+      stage_t st[RPW];
+      auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
+        const int s0 = tile * kTile + wave_u * RPW;
 #pragma unroll
-        for (int jj = 0; jj < RPW; ++jj)
-          st[jj] = *(const u32x2*)(row_src(tile, wave_u * RPW + jj) + lane * 8);
+        for (int q = 0; q < RPW / 4; ++q) {
+          const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
+        }
+      };
+      auto load_row = [&](int tile, int jj, const int (&codes)[RPW]) {
+        const int s0 = tile * kTile + wave_u * RPW;
+        int code = __builtin_amdgcn_readfirstlane(codes[jj]);
+        code = (s0 + jj < n_act) ? code : last_code;
+        const uint8_t* base = code < 0 ? p.comp : p.swa;
+        const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+        st[jj] = *(const stage_t*)(row + lane_off);
       };
       auto store = [&](int tile) {
-        uint8_t* dst = kv_lds + (tile & 1) * kTileBytes;
+        uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
 #pragma unroll
-        for (int jj = 0; jj < RPW; ++jj)
-          *(u32x4*)(dst + (wave * RPW + jj) * kRowPitch + lane * 16) =
-              widen_e4m3fn_x8(st[jj]);
+        for (int jj = 0; jj < RPW; ++jj) {
+          u32x4 v;
+          if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
+          else v = st[jj];
+          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
+        }
       };
-      if (ntiles > 0) {
-        load(0);
-        store(0);
+      // prologue: tiles 0 .. NSTAGE-2 into their stages
+      for (int tl = 0; tl < min(NSTAGE - 1, ntiles); ++tl) {
+        int codes[RPW];
+        fetch_codes(tl, codes);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) load_row(tl, jj, codes);
+        store(tl);
       }
       for (int it = 0; it < ntiles; ++it) {
-        __syncthreads();            // tile it stored; tile it-1 done
-        if (restart_flag) {
-          again = true;
-          break;
-        }
-        if (it + 1 < ntiles) load(it + 1);
-        attend(kv_lds + (it & 1) * kTileBytes, min(kTile, n_act - it * kTile));
-        if (it + 1 < ntiles) store(it + 1);
+        __syncthreads();            // tile it stored by every wave; it-1 done
+        const int nxt = it + NSTAGE - 1;
+        const bool do_load = nxt < ntiles;
+        int codes[RPW];
+        fetch_codes(do_load ? nxt : it, codes);
+        const f32x16 sv = qk(stage(it), [&](int q) {
+#pragma unroll
+          for (int r = 0; r < RPW / 8; ++r)
+            if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
+        });
+        bf16x8 pf[2];
+        softmax(sv, n_in(it), pf);
+        pv(stage(it), pf);
+        if (do_load) store(nxt);
       }
     }
-    // a restart asked for by the segment's last tile
+    // did any wave's tile outgrow its reference max?
+    if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
     __syncthreads();
-    if (restart_flag) again = true;
+    again = restart_flag != 0;
   }
   if (again) {
     // Rare: start the split over with the raised reference maxima.
     wait_vmcnt<0>();                // no row gather may still be landing
     __syncthreads();
     if (threadIdx.x == 0) restart_flag = 0;
+    need_sticky = false;
     l_run = 0.f;
 #pragma unroll
     for (int db = 0; db < 16; ++db)
