@@ -12,24 +12,28 @@
 //
 // Kernel design (ours, for CDNA4; the pages' TRTLLM-gen / CuTe kernels are
 // prior art only):
-//  * One workgroup of 4 wave64s per (token, split).  All H heads of the
-//    token live in the workgroup, so each gathered row is read from HBM
-//    once per (token, split) and reused by every head.  Wave w owns heads
-//    [w*H/4, (w+1)*H/4): 16 heads (H=64) or 32 heads (H=128).
-//  * The split's table columns are compacted in LDS first (masked, -1,
-//    truncated and out-of-range slots are dropped), so tiles are dense.
-//  * Rows are gathered 32 at a time into a double-buffered, XOR-swizzled
-//    row-major LDS tile (FP8 rows are widened to BF16 on the way; every
-//    E4M3FN value is exactly a BF16 value).
-//  * S^T = K * Q^T on MFMA 16x16x32 BF16 (A = tile rows from LDS, B = the
-//    wave's Q held in registers).  The accumulator layout of S^T puts one
-//    head per lane column, which is exactly the B-operand layout P^T needs
-//    for O^T = V^T * P^T, so softmax probabilities go to the second MFMA
-//    without any cross-lane shuffle.
-//  * Online softmax in base 2 with a lazily refreshed running max (the
-//    reference max only moves when a tile's max exceeds it by more than 8,
-//    so O is rarely rescaled); the final normalisation uses the same
-//    reference, so the result is exact up to rounding.
+//  * One workgroup of 4 wave64s (2 at H=64) per (token, split), one wave per
+//    SIMD.  All H heads of the token live in the workgroup, so each gathered
+//    row is read from HBM once per (token, split) and reused by every head.
+//  * The split's table columns are compacted first (masked, -1, truncated
+//    and out-of-range slots are dropped), so tiles are dense.
+//  * Rows are gathered 32 at a time into row-major LDS tiles with a padded
+//    pitch (conflict-free row and transposed reads), by LDS-DMA for BF16
+//    rows and through registers for FP8 rows (widened to BF16 on the way;
+//    every E4M3FN value is exactly a BF16 value).
+//  * S^T = K Q^T on MFMA 32x32x16 BF16 (A = tile rows from LDS, B = 32
+//    heads of Q held in registers).  The accumulator layout of S^T is the
+//    B-operand layout P^T needs for O^T = V^T P^T, so probabilities go to
+//    the second MFMA without a cross-lane shuffle; V^T comes from LDS with
+//    transposing reads.
+//  * Online softmax in base 2 against a reference max that is set by the
+//    first tile and left alone; a tile exceeding it by more than 2^64 makes
+//    the split start over with the higher reference, so O is never rescaled
+//    and the result is exact up to rounding.
+//  * decode_kernel (H=64, and FP8 rows): wave w computes S and O for its
+//    own 32 heads.  decode_hd_kernel (H=128, BF16 rows): wave w computes S
+//    for 32 heads but O for a quarter of the output dims of all heads, with
+//    P exchanged through LDS (see there).
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
 //    merges them.
@@ -180,7 +184,11 @@ __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
                                               uint32_t lane_off,
                                               uint32_t lds_addr) {
   uint32_t saved;
+  // s_nop 4: the row address may have just been written by a VALU
+  // (v_readlane / v_readfirstlane), and a VMEM read of a VALU-written SGPR
+  // needs 5 wait states; s_nop 0: M0 written by SALU before LDS-DMA.
   asm volatile(
+      "s_nop 4\n\t"
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
       "s_nop 0\n\t"
@@ -628,6 +636,458 @@ void decode_kernel(DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// split kernel, H = 128 with BF16 rows: heads for S, output dims for O
+// ---------------------------------------------------------------------------
+//
+// Four waves.  Wave w computes S^T and the softmax of heads [32w, 32w+32)
+// (a 32 x 32 S^T tile per 32-row KV tile, as above), but accumulates O^T
+// for the output dims [128w, 128w+128) of all 128 heads.  P^T is exchanged
+// through LDS in exactly the B-operand layout the O^T MFMAs take, so the
+// exchange is one 16-byte store and one 16-byte load per lane and head
+// block.  Each wave then reads only its quarter of every V tile with the
+// (half-rate) transposing LDS reads.  O^T of tile i-1 is computed while the
+// softmax of tile i runs on the VALU: the two are independent, so the
+// exponentials fill the gaps between O^T MFMAs.
+//
+// With one wave per SIMD nothing else can issue MFMAs while a wave is busy
+// elsewhere, so the per-row gather work is kept small: the compacted slot
+// list is padded to whole tiles, a tile's row addresses are computed by
+// one VALU pass (one row per lane) and read out into SGPRs, and each row
+// costs one load instruction.
+
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
+template <bool Q_FP8, bool SPLIT>
+__global__ __launch_bounds__(256, 1)
+void decode_hd_kernel(DecodeParams p) {
+  constexpr int NW = 4, H = 128, NT = 256;
+  constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
+  // LDS tiles: i-1 (read by O^T), i (S^T), i+1 and i+2 (landing).
+  constexpr int NSTAGE = 4;
+  constexpr int kSegHd = 2048;           // table columns per pass
+  constexpr int CPT = kSegHd / NT;        // columns per thread in compaction
+  constexpr int NHB = H / 32;             // head blocks
+  constexpr int NDB = kD / NW / 32;       // 32-dim blocks of O per wave
+  constexpr int kPBuf = NHB * 2 * 64;     // P^T of one tile, in u32x4
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
+  __shared__ __attribute__((aligned(16))) u32x4 p_lds[2 * kPBuf];
+  // code of each active row of the segment (SWA: row, compressed: row with
+  // bit 31 set), padded with the last active row up to a whole tile
+  __shared__ __attribute__((aligned(16))) int32_t slots[kSegHd + kTile];
+  __shared__ float inv_lds[H];
+  __shared__ int32_t wave_cnt[NW];
+  __shared__ int32_t restart_flag;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31;
+  const int kg = lane >> 5;
+
+  // XCD-aware work mapping (see decode_kernel).
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int q8 = nblk >> 3, r8 = nblk & 7;
+  const int item = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
+  const int t = item / p.S;
+  const int s = item - t * p.S;
+  const int head = wave * 32 + l32;       // head of this lane's S^T column
+
+  // Loads in the order their results are needed: topk_len, the first
+  // segment's table entries (fetched before topk_len is known; columns past
+  // it are dropped in the compaction), then Q.  vmcnt retires in order, so
+  // waiting for the table entries does not wait for Q.
+  const int c_begin = s * p.split_cols;
+  const int c_cap = min(p.K, c_begin + p.split_cols);
+  const int len_raw = p.topk_lens ? p.topk_lens[t] : p.K;
+  int rv[CPT];
+  auto load_idx = [&](int seg0, int seg_hi) {
+    const int cb = seg0 + threadIdx.x * CPT;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      rv[k] = (cb + k < seg_hi) ? p.indices[(int64_t)t * p.index_row_stride + cb + k] : -1;
+  };
+  load_idx(c_begin, min(c_cap, c_begin + kSegHd));
+  __builtin_amdgcn_sched_barrier(0);
+
+  bf16x8 qf[32];
+  {
+    const size_t qrow = ((size_t)t * H + head) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      const int d0 = kk * 16 + kg * 8;
+      u32x4 v;
+      if constexpr (Q_FP8)
+        v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
+      else
+        v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  __builtin_amdgcn_sched_barrier(0);
+  if (p.validate && threadIdx.x == 0 && s == 0 && (len_raw < 0 || len_raw > p.K))
+    record_error(p.err, 2, t, -1);
+  const int len = min(max(len_raw, 0), p.K);
+  const int c_end = min(len, c_cap);
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  // O^T: o[db][hb] holds dims 128w + 32db + 8(i/4) + 4kg + i%4 of head
+  // 32hb + l32.
+  f32x16 o[NDB][NHB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+
+  const int qk_off = l32 * kRowPitch + kg * 16;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int tr_off = (4 * (grp >> 1) + (i16 >> 2)) * kRowPitch +
+                     (16 * (grp & 1) + 4 * (i16 & 3)) * 2 + wave * (NDB * 64);
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+
+  if (threadIdx.x == 0) restart_flag = 0;
+  bool need_sticky = false;
+
+  constexpr int kLead = 4;
+  auto qk = [&](const uint8_t* tb, auto&& every) -> f32x16 {
+    bf16x8 a[kLead];
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
+    f32x16 acc;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
+      else mfma_qk(acc, a[kk % kLead], qf[kk]);
+      if (kk + kLead < 32)
+        a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
+      __builtin_amdgcn_sched_barrier(0);
+      every(kk);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return acc;
+  };
+
+  // One step block: O^T += V^T P^T for the previous tile (DO_PV) with the
+  // softmax of the current tile's S^T spread over its 32 MFMAs.  The
+  // softmax writes P^T of the current tile to `pw`.  Rows past the end of a
+  // ragged tile arrive with S^T = -inf and get probability 0.  Only one
+  // instance of this block updates O, so O keeps one register assignment.
+  auto step_block = [&](auto do_pv, const uint8_t* vt, const u32x4* pr,
+                        f32x16 sv, u32x4* pw, auto&& every) {
+    constexpr bool kPV = decltype(do_pv)::value;
+    constexpr int kVLead = 2;
+    auto vfrag = [&](int f) -> bf16x8 {   // f = 4h + db: rows 16h.., dims block db
+      const uint8_t* vb = vt + tr_off + (16 * (f >> 2)) * kRowPitch + (f & 3) * 64;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+      return __builtin_bit_cast(bf16x8,
+                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    auto pfrag = [&](int h, int hb) -> bf16x8 {
+      return __builtin_bit_cast(bf16x8, pr[(hb * 2 + h) * 64 + lane]);
+    };
+    // P^T operands of the current 16-row half: P^T(1, hb) replaces
+    // P^T(0, hb) right after its last use, four MFMAs before it is needed.
+    bf16x8 pfr[NHB];
+    bf16x8 vfr[kVLead];
+    if constexpr (kPV) {
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) pfr[hb] = pfrag(0, hb);
+#pragma unroll
+      for (int f = 0; f < kVLead; ++f) vfr[f] = vfrag(f);
+    }
+    float smax = 0.f, neg_m = 0.f, lsum = 0.f, pprev = 0.f;
+    u32x4 pk[2];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kPV) {
+        const int f = k >> 2, hb = k & 3;
+        o[f & 3][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            vfr[f % kVLead], pfr[hb], o[f & 3][hb], 0, 0, 0);
+        if (hb == 3 && f + kVLead < 8) vfr[f % kVLead] = vfrag(f + kVLead);
+        if (f == 3) pfr[hb] = pfrag(1, hb);
+      }
+      if (k == 0) {
+        smax = sv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) smax = fmaxf(smax, sv[i]);
+      } else if (k == 1) {
+#pragma unroll
+        for (int i = 8; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+        smax = max_with_other_half(smax);
+      } else if (k == 2) {
+        // The reference max is set by the first tile and then left alone,
+        // so O is never rescaled inside the loop (see decode_kernel).
+        const float tmax = smax * p.scale_log2;     // scale_log2 > 0
+        m_run = (m_run == -INFINITY) ? tmax : m_run;
+        const bool need = tmax > m_run + kRefSlack;
+        m_run = need ? tmax : m_run;
+        need_sticky |= need;
+        neg_m = -m_run;
+      } else if (k >= 3 && k < 19) {
+        const int i = k - 3;
+        const float pi = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, neg_m));
+        lsum += pi;
+        if (i & 1) pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(pprev, pi);
+        pprev = pi;
+      } else if (k == 19) {
+        pw[(wave * 2 + 0) * 64 + lane] = pk[0];
+        pw[(wave * 2 + 1) * 64 + lane] = pk[1];
+        l_run += lsum;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      every(k);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto no_hook = [](int) {};
+
+  bool again;
+  bool first_seg = true;
+  do {
+  again = false;
+  for (int seg0 = c_begin; seg0 < c_end && !again; seg0 += kSegHd) {
+    const int seg1 = min(c_end, seg0 + kSegHd);
+
+    // ---- compact the active slots of this segment into row addresses ------
+    // Thread i takes CPT consecutive columns; all its index loads are in
+    // flight together.  Slot order is column order.
+    __syncthreads();   // the previous segment no longer reads slots[] / tiles
+    if (!first_seg) load_idx(seg0, seg1);
+    first_seg = false;
+    const int cb = seg0 + threadIdx.x * CPT;
+    uint32_t actm = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = cb + k;
+      const int r = rv[k];
+      if (r != -1 && c < seg1) {
+        const int64_t rows = (c < kSwaColumns) ? p.swa_rows : p.comp_rows;
+        if (r >= 0 && (int64_t)r < rows) actm |= 1u << k;
+        else if (p.validate) record_error(p.err, 1, t, c);
+      }
+    }
+    const int cnt = __popc(actm);
+    int incl = cnt;                      // inclusive prefix over the wave
+#pragma unroll
+    for (int o2 = 1; o2 < 64; o2 <<= 1) {
+      const int y = __shfl_up(incl, o2);
+      incl += (lane >= o2) ? y : 0;
+    }
+    if (lane == 63) wave_cnt[wave] = incl;
+    __syncthreads();
+    int pos = incl - cnt, n_act = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int cw = wave_cnt[w2];
+      pos += (w2 < wave) ? cw : 0;
+      n_act += cw;
+    }
+    int last = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if ((actm >> k) & 1u) {
+        last = (cb + k < kSwaColumns) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
+        slots[pos++] = last;
+      }
+    }
+    // the owner of the last active slot pads the tail of the last tile
+    const int ntiles = (n_act + kTile - 1) / kTile;
+    if (cnt > 0 && pos == n_act) {
+      for (int i = n_act; i < ntiles * kTile; ++i) slots[i] = last;
+    }
+    __syncthreads();
+    auto n_in = [&](int tile) { return min(kTile, n_act - tile * kTile); };
+    auto stage = [&](int tile) -> const uint8_t* {
+      return kv_lds + (tile % NSTAGE) * kTileBytes;
+    };
+    // The wave's RPW row addresses of a tile, in SGPRs: lane j converts
+    // the code of row j on the VALU, then each address is read out of its
+    // lane (a few instructions per tile instead of a scalar multiply chain
+    // per row).
+    auto fetch_rows = [&](int tile, const uint8_t* (&rows)[RPW]) {
+      const int code = slots[tile * kTile + wave_u * RPW + (lane & (RPW - 1))];
+      const uint8_t* base = code < 0 ? p.comp : p.swa;
+      const uint64_t a = (uint64_t)(uintptr_t)(
+          base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
+      const int alo = (int)(uint32_t)a, ahi = (int)(uint32_t)(a >> 32);
+#pragma unroll
+      for (int jj = 0; jj < RPW; ++jj) {
+        // (readlane returns int: widen through uint32_t, not with sign
+        // extension)
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(alo, jj);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(ahi, jj);
+        rows[jj] = (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+      }
+    };
+    auto mask_tail = [&](f32x16& sv, int it) {
+      const int nt = n_in(it);
+      if (nt < kTile) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sv[i] = (tile_row_of_reg(i, kg) < nt) ? sv[i] : -INFINITY;
+      }
+    };
+
+    const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
+    auto issue_row = [&](int tile, int jj, const uint8_t* row) {
+      const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
+                           (uint32_t)((wave_u * RPW + jj) * kRowPitch);
+      lds_dma_row16(row, lane_off, dst);
+    };
+    // Q has landed before the first row gather goes out: the compiler's own
+    // waits for Q count only its loads, so they would otherwise also wait
+    // for the gathers issued after Q.
+    if (ntiles > 0) wait_vmcnt<0>();
+
+    if (ntiles > 0) {
+      // LDS-DMA gather, two tiles ahead.
+      const uint8_t* rows[RPW];
+      for (int tl = 0; tl < min(2, ntiles); ++tl) {
+        fetch_rows(tl, rows);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) issue_row(tl, jj, rows[jj]);
+      }
+      fetch_rows(min(2, ntiles - 1), rows);
+      // The RPW rows of tile it+2 go out during the S^T MFMAs of tile it.
+      auto qk_tile = [&](int it, bool do_issue) -> f32x16 {
+        f32x16 sv = qk(stage(it), [&](int kk) {
+          if (do_issue && (kk & 3) == 3) issue_row(it + 2, kk >> 2, rows[kk >> 2]);
+        });
+        mfma_qk_drain(sv);
+        mask_tail(sv, it);
+        return sv;
+      };
+      // Wait until this wave's rows of tile it landed (the rows of tile
+      // it+1 may still be in flight), then for every wave's: the barrier
+      // also orders P^T of tile it-1 before its readers and frees the stage
+      // of tile it-2 for tile it+2.
+      auto land = [&](int it) {
+        if (it + 1 < ntiles) wait_vmcnt<RPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+      };
+      land(0);
+      {
+        const bool di = 2 < ntiles;
+        step_block(BoolC<false>{}, kv_lds, p_lds, qk_tile(0, di), p_lds, no_hook);
+        if (di) fetch_rows(min(3, ntiles - 1), rows);
+      }
+      for (int it = 1; it <= ntiles; ++it) {
+        if (it < ntiles) land(it);
+        else __syncthreads();
+        const bool di = it + 2 < ntiles;
+        f32x16 sv;
+        if (it < ntiles) {
+          sv = qk_tile(it, di);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
+        }
+        step_block(BoolC<true>{}, stage(it - 1), p_lds + ((it - 1) & 1) * kPBuf, sv,
+                   p_lds + (it & 1) * kPBuf, no_hook);
+        if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
+      }
+    }
+    if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
+    __syncthreads();
+    again = restart_flag != 0;
+  }
+  if (again) {
+    // Rare: start the split over with the raised reference maxima.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) restart_flag = 0;
+    need_sticky = false;
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+  }
+  } while (again);
+
+  // ---- epilogue: the head owner finishes its head's normaliser ------------
+  {
+    float l = l_run + __shfl_xor(l_run, 32);
+    float m = m_run;
+    float inv, lse;
+    if constexpr (SPLIT) {
+      inv = (l > 0.f) ? p.bmm2 / l : 0.f;
+      lse = (l > 0.f) ? m + fast_log2(l) : -INFINITY;
+    } else {
+      float fac = 1.f;
+      if (p.sinks) {
+        const float sl = p.sinks[head] * kLog2e;
+        const float mm = fmaxf(m, sl);
+        fac = fast_exp2(m - mm);       // 0 when nothing was active (m = -inf)
+        l = l * fac + fast_exp2(sl - mm);
+        m = mm;
+      }
+      inv = (l > 0.f) ? fac * p.bmm2 / l : 0.f;
+      lse = (l > 0.f) ? p.lse_scale * (m + fast_log2(l)) : -INFINITY;
+    }
+    if (kg == 0) {
+      inv_lds[head] = inv;
+      if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
+      else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
+    }
+  }
+  __syncthreads();
+  // ---- O goes out through LDS as whole 1 KB head rows ---------------------
+  // (the tiles are no longer in use).  Two passes of 64 heads: every wave
+  // writes its 128 dims of each head, then each wave stores whole rows.
+  constexpr int kOutPitch = kD * 2 + 16;
+  static_assert(64 * kOutPitch <= NSTAGE * kTileBytes, "epilogue staging");
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      const int hb = 2 * pass + hq;
+      const float inv = inv_lds[hb * 32 + l32];
+      uint8_t* rowp = kv_lds + (hq * 32 + l32) * kOutPitch + wave * (NDB * 64) + kg * 8;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          u32x2 w;
+          w[0] = pack_bf16x2(o[db][hb][4 * a] * inv, o[db][hb][4 * a + 1] * inv);
+          w[1] = pack_bf16x2(o[db][hb][4 * a + 2] * inv, o[db][hb][4 * a + 3] * inv);
+          *(u32x2*)(rowp + db * 64 + a * 16) = w;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r * NW + wave;
+      const int hh = pass * 64 + row;
+      const u32x4 v = *(const u32x4*)(kv_lds + row * kOutPitch + lane * 16);
+      uint16_t* dst;
+      if constexpr (SPLIT)
+        dst = p.mid_out + (((size_t)t * H + hh) * p.S + s) * kD;
+      else
+        dst = (uint16_t*)p.out + ((size_t)t * H + hh) * kD;
+      *(u32x4*)(dst + lane * 8) = v;
+    }
+    if (pass == 0) __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // combine kernel: one wave per (token, head); lane owns 8 output dims
 // ---------------------------------------------------------------------------
 
@@ -674,6 +1134,16 @@ __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
 
+template <bool QF>
+hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.T * p.S));
+  if (p.S > 1)
+    hipLaunchKernelGGL((decode_hd_kernel<QF, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_hd_kernel<QF, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int NW, bool QF, bool KF>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
@@ -696,8 +1166,8 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
     if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
     return launch_decode_t<2, false, true>(p, stream);
   }
-  if (!qf && !kf) return launch_decode_t<4, false, false>(p, stream);
-  if (qf && kf) return launch_decode_t<4, true, true>(p, stream);
+  if (!kf) return launch_decode_hd<false>(p, stream);   // Q FP8 needs FP8 rows
+  if (qf) return launch_decode_t<4, true, true>(p, stream);
   return launch_decode_t<4, false, true>(p, stream);
 }
 
