@@ -780,32 +780,36 @@ void decode_hd_kernel(DecodeParams p) {
   // softmax writes P^T of the current tile to `pw`.  Rows past the end of a
   // ragged tile arrive with S^T = -inf and get probability 0.  Only one
   // instance of this block updates O, so O keeps one register assignment.
+  // O^T operands from LDS: V^T fragment f = 4h + db (rows 16h.., dims
+  // block db of this wave) and P^T fragment (h, hb).
+  constexpr int kVLead = 2;
+  auto vfrag = [&](const uint8_t* vt, int f) -> bf16x8 {
+    const uint8_t* vb = vt + tr_off + (16 * (f >> 2)) * kRowPitch + (f & 3) * 64;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(vb));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pfrag = [&](const u32x4* pr, int h, int hb) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, pr[(hb * 2 + h) * 64 + lane]);
+  };
+  // The first O^T operands of a block are read before the S^T MFMAs that
+  // precede it, so the block does not start with an LDS round trip.
+  auto pv_prefetch = [&](const uint8_t* vt, const u32x4* pr, bf16x8 (&pfr)[NHB],
+                         bf16x8 (&vfr)[kVLead]) {
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) pfr[hb] = pfrag(pr, 0, hb);
+#pragma unroll
+    for (int f = 0; f < kVLead; ++f) vfr[f] = vfrag(vt, f);
+  };
   auto step_block = [&](auto do_pv, const uint8_t* vt, const u32x4* pr,
+                        bf16x8 (&pfr)[NHB], bf16x8 (&vfr)[kVLead],
                         f32x16 sv, u32x4* pw, auto&& every) {
     constexpr bool kPV = decltype(do_pv)::value;
-    constexpr int kVLead = 2;
-    auto vfrag = [&](int f) -> bf16x8 {   // f = 4h + db: rows 16h.., dims block db
-      const uint8_t* vb = vt + tr_off + (16 * (f >> 2)) * kRowPitch + (f & 3) * 64;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 __attribute__((address_space(3)))*)(vb));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
-      return __builtin_bit_cast(bf16x8,
-                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    auto pfrag = [&](int h, int hb) -> bf16x8 {
-      return __builtin_bit_cast(bf16x8, pr[(hb * 2 + h) * 64 + lane]);
-    };
     // P^T operands of the current 16-row half: P^T(1, hb) replaces
     // P^T(0, hb) right after its last use, four MFMAs before it is needed.
-    bf16x8 pfr[NHB];
-    bf16x8 vfr[kVLead];
-    if constexpr (kPV) {
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) pfr[hb] = pfrag(0, hb);
-#pragma unroll
-      for (int f = 0; f < kVLead; ++f) vfr[f] = vfrag(f);
-    }
     float smax = 0.f, neg_m = 0.f, lsum = 0.f, pprev = 0.f;
     u32x4 pk[2];
 #pragma unroll
@@ -815,8 +819,8 @@ void decode_hd_kernel(DecodeParams p) {
         const int f = k >> 2, hb = k & 3;
         o[f & 3][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             vfr[f % kVLead], pfr[hb], o[f & 3][hb], 0, 0, 0);
-        if (hb == 3 && f + kVLead < 8) vfr[f % kVLead] = vfrag(f + kVLead);
-        if (f == 3) pfr[hb] = pfrag(1, hb);
+        if (hb == 3 && f + kVLead < 8) vfr[f % kVLead] = vfrag(vt, f + kVLead);
+        if (f == 3) pfr[hb] = pfrag(pr, 1, hb);
       }
       if (k == 0) {
         smax = sv[0];
@@ -981,13 +985,17 @@ void decode_hd_kernel(DecodeParams p) {
       land(0);
       {
         const bool di = 2 < ntiles;
-        step_block(BoolC<false>{}, kv_lds, p_lds, qk_tile(0, di), p_lds, no_hook);
+        bf16x8 pfr[NHB], vfr[kVLead];
+        step_block(BoolC<false>{}, kv_lds, p_lds, pfr, vfr, qk_tile(0, di), p_lds, no_hook);
         if (di) fetch_rows(min(3, ntiles - 1), rows);
       }
       for (int it = 1; it <= ntiles; ++it) {
         if (it < ntiles) land(it);
         else __syncthreads();
         const bool di = it + 2 < ntiles;
+        const u32x4* pr = p_lds + ((it - 1) & 1) * kPBuf;
+        bf16x8 pfr[NHB], vfr[kVLead];
+        pv_prefetch(stage(it - 1), pr, pfr, vfr);
         f32x16 sv;
         if (it < ntiles) {
           sv = qk_tile(it, di);
@@ -995,7 +1003,7 @@ void decode_hd_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
         }
-        step_block(BoolC<true>{}, stage(it - 1), p_lds + ((it - 1) & 1) * kPBuf, sv,
+        step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
                    p_lds + (it & 1) * kPBuf, no_hook);
         if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
       }
