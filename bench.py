@@ -11,8 +11,15 @@ A step is one sparse_mla_decode call (planner + split kernel [+ combine]).
 Each launch is bracketed by HIP events on the stream it runs on, so the
 average launch duration, gathered bytes and FLOPs give the roofline numbers.
 
+Besides the headline numbers the line carries: the pure-gather rate on the
+same tables (sparse_mla_gather_only: compaction and row loads only, the
+attainable gather bandwidth), a cold-cache rate (a 1 GiB write between
+launches evicts L2 and MALL), and with --sweep the per-T numbers for
+T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
+back-to-back launches.
+
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
---no-cpu-baseline, --sweep (adds per-T numbers for T in 1,4,8,64,256).
+--no-cpu-baseline, --sweep.
 """
 
 import argparse
@@ -81,6 +88,49 @@ def time_launches(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
     return start.elapsed_time(end), per
+
+
+def time_cold(fn, iters, stream):
+    """Median per-launch ms of fn() with a 1 GiB device write before each
+    launch (outside the timed window), so L2 and MALL start cold."""
+    import torch
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(iters):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    times.sort()
+    return times[len(times) // 2]
+
+
+def time_graph(fn, launches=20, replays=5):
+    """Per-launch ms of fn() captured `launches` times into one HIP graph."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(launches):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (launches * replays)
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -170,6 +220,12 @@ def main():
                    lse_scale=w.lse_scale, plan=plan, workspace=ws, stream=stream)
 
     total_ms, per = time_launches(step, args.steps, args.warmup, stream)
+
+    def gather_step():
+        lib.gather_only(w.q, w.swa_pool, w.comp_pool, w.indices,
+                        topk_lens=w.topk_lens, plan=plan, stream=stream)
+    _, gper = time_launches(gather_step, max(args.steps // 2, 5), 3, stream)
+    cold_ms = time_cold(step, 10, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     gathered = int(n_act.sum()) * ROW_BYTES
@@ -209,6 +265,9 @@ def main():
         "tflops": round(achieved_tflops, 1),
         "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
         "avg_launch_ms": round(avg_launch_ms, 4),
+        "gather_only_GBps": round(gathered / (sum(gper) / len(gper) * 1e-3) / 1e9, 1),
+        "decode_vs_gather_only": round((sum(gper) / len(gper)) / avg_launch_ms, 4),
+        "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
         "plan": plan.as_dict(),
         "roofline": roofline,
     }
@@ -225,7 +284,7 @@ def main():
                 lib.decode(w.q[:t], w.swa_pool, w.comp_pool, w.indices[:t], o2,
                            out_lse=l2, topk_lens=w.topk_lens[:t], sinks=w.sinks,
                            bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
-                           plan=p, workspace=wsp, stream=stream)
+                           plan=p, workspace=wsp)   # current stream (graph capture)
             tot, pl = time_launches(st, 50, 5, stream)
             g = int(n_act[:t].sum()) * ROW_BYTES
             avg = sum(pl) / len(pl)
@@ -235,6 +294,10 @@ def main():
                              "num_splits": p.num_splits,
                              "roofline_frac": round(g / (HBM_PEAK_GBPS * 1e9) /
                                                     (avg * 1e-3), 4)}
+            if t <= 8:
+                gms = time_graph(st)
+                sweep[str(t)]["graph_launch_us"] = round(gms * 1e3, 2)
+                sweep[str(t)]["graph_gathered_GBps"] = round(g / (gms * 1e-3) / 1e9, 1)
         result["sweep"] = sweep
     if args.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1)

@@ -180,6 +180,17 @@ int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
 int sparse_mla_decode(const smla_decode_args* args, const smla_plan* plan,
                       smla_stream_t stream);
 
+/* Measurement aid (not part of the method): run only the table compaction
+ * and the row gather of sparse_mla_decode on the same arguments and plan,
+ * with no arithmetic and no output, to give the attainable gathered-row
+ * bandwidth on these exact tables (the survey's companion pure-gather
+ * benchmark).  Same argument checks as sparse_mla_decode except that out,
+ * out_lse and the workspace are not used; only H = 128 with BF16 q and
+ * rows is supported (else SMLA_ERR_UNSUPPORTED_SHAPE / _DTYPE).
+ * Asynchronous on "stream"; no allocation. */
+int sparse_mla_gather_only(const smla_decode_args* args, const smla_plan* plan,
+                           smla_stream_t stream);
+
 /* Merge split partials (FlashInfer cake_* "mid_out"/"mid_lse" and the
  * combine of msa_sparse_decode_attention "force_fused"):
  *   mid_out [T, H, split_stride, 512] BF16 and mid_lse [T, H, split_stride]

@@ -159,14 +159,22 @@ int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
   return SMLA_OK;
 }
 
-int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
-                      smla_stream_t stream_handle) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by sparse_mla_decode and sparse_mla_gather_only,
+// and the kernel parameters they resolve to.  *plan is replaced by
+// *local when the caller passed none.  Returns SMLA_OK or a status.
+int prepare_call(const smla_decode_args* a, const smla_plan*& plan, smla_plan* local,
+                 bool with_outputs, smla::DecodeParams* p, Layout* L) {
   if (!a) return SMLA_ERR_INVALID_ARG;
   if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
   if (a->H != 64 && a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (!dtype_pair_ok(a->q_dtype, a->kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
   if (a->T == 0) return SMLA_OK;
-  if (!a->q || !a->swa_pool || !a->indices || !a->out) return SMLA_ERR_INVALID_ARG;
+  if (!a->q || !a->swa_pool || !a->indices || (with_outputs && !a->out))
+    return SMLA_ERR_INVALID_ARG;
   if (a->K > smla::kSwaColumns && !a->compressed_pool) return SMLA_ERR_INVALID_ARG;
   if (a->swa_rows < 0 || a->compressed_rows < 0) return SMLA_ERR_INVALID_ARG;
   if ((int64_t)a->T * a->H > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
@@ -176,63 +184,77 @@ int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
   if (idx_stride < a->K) return SMLA_ERR_INVALID_ARG;
   if (a->cum_seq_lens_q && a->num_requests < 1) return SMLA_ERR_INVALID_ARG;
   const int kv_elem = a->kv_dtype == SMLA_DTYPE_FP8_E4M3FN ? 1 : 2;
-  if (!aligned(a->q, 16) || !aligned(a->out, 16) || !aligned(a->swa_pool, 16) ||
+  if (!aligned(a->q, 16) || (with_outputs && !aligned(a->out, 16)) ||
+      !aligned(a->swa_pool, 16) ||
       (a->compressed_pool && !aligned(a->compressed_pool, 16)) ||
       (row_stride * kv_elem) % 16 != 0 || !aligned(a->indices, 4))
     return SMLA_ERR_MISALIGNED;
 
-  smla_plan local;
   if (!plan) {
     const int st = sparse_mla_plan_splits(a->T, a->H, a->K, a->q_dtype, a->kv_dtype,
-                                          0, 0, 0, &local);
+                                          0, 0, 0, local);
     if (st != SMLA_OK) return st;
-    plan = &local;
+    plan = local;
   }
   if (!plan_ok(plan, a->K)) return SMLA_ERR_BAD_PLAN;
   const int S = plan->num_splits;
   if ((int64_t)a->T * S > INT_MAX) return SMLA_ERR_INVALID_ARG;
 
-  const bool validate = (a->flags & SMLA_FLAG_VALIDATE_INDICES) != 0;
-  const Layout L = layout_for(S, a->T, a->H, a->flags);
-  if (L.total > 0) {
+  const bool validate = with_outputs && (a->flags & SMLA_FLAG_VALIDATE_INDICES) != 0;
+  *L = layout_for(with_outputs ? S : 1, a->T, a->H, validate ? a->flags : 0);
+  if (L->total > 0) {
     if (!a->workspace) return SMLA_ERR_WORKSPACE_TOO_SMALL;
-    if (a->workspace_bytes < L.total) return SMLA_ERR_WORKSPACE_TOO_SMALL;
+    if (a->workspace_bytes < L->total) return SMLA_ERR_WORKSPACE_TOO_SMALL;
     if (!aligned(a->workspace, 256)) return SMLA_ERR_MISALIGNED;
   }
 
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
-  int32_t* err = validate ? reinterpret_cast<int32_t*>(ws) : nullptr;
-  if (validate && smla::launch_clear_error(err, stream) != hipSuccess)
-    return SMLA_ERR_HIP;
-
-  smla::DecodeParams p{};
-  p.q = a->q;
-  p.swa = static_cast<const uint8_t*>(a->swa_pool);
-  p.comp = static_cast<const uint8_t*>(a->compressed_pool);
-  p.swa_rows = a->swa_rows;
-  p.comp_rows = a->compressed_pool ? a->compressed_rows : 0;
-  p.row_stride_bytes = row_stride * kv_elem;
-  p.indices = a->indices;
-  p.index_row_stride = idx_stride;
-  p.topk_lens = a->topk_lens;
-  p.sinks = a->sinks;
-  p.scale_log2 = (float)((double)a->bmm1_scale * 1.4426950408889634);
-  p.bmm2 = a->bmm2_scale;
-  p.lse_scale = a->lse_scale;
-  p.out = a->out;
-  p.out_lse = a->out_lse;
-  p.err = err;
-  p.T = a->T;
-  p.H = a->H;
-  p.K = a->K;
-  p.S = S;
-  p.split_cols = plan->chunks_per_split * plan->chunk_cols;
-  p.validate = validate ? 1 : 0;
-  if (S > 1) {
-    p.mid_lse = reinterpret_cast<float*>(ws + L.mid_lse);
-    p.mid_out = reinterpret_cast<uint16_t*>(ws + L.mid_out);
+  *p = smla::DecodeParams{};
+  p->q = a->q;
+  p->swa = static_cast<const uint8_t*>(a->swa_pool);
+  p->comp = static_cast<const uint8_t*>(a->compressed_pool);
+  p->swa_rows = a->swa_rows;
+  p->comp_rows = a->compressed_pool ? a->compressed_rows : 0;
+  p->row_stride_bytes = row_stride * kv_elem;
+  p->indices = a->indices;
+  p->index_row_stride = idx_stride;
+  p->topk_lens = a->topk_lens;
+  p->sinks = a->sinks;
+  p->scale_log2 = (float)((double)a->bmm1_scale * 1.4426950408889634);
+  p->bmm2 = a->bmm2_scale;
+  p->lse_scale = a->lse_scale;
+  p->out = a->out;
+  p->out_lse = a->out_lse;
+  p->err = validate ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  p->T = a->T;
+  p->H = a->H;
+  p->K = a->K;
+  p->S = S;
+  p->split_cols = plan->chunks_per_split * plan->chunk_cols;
+  p->validate = validate ? 1 : 0;
+  if (with_outputs && S > 1) {
+    p->mid_lse = reinterpret_cast<float*>(ws + L->mid_lse);
+    p->mid_out = reinterpret_cast<uint16_t*>(ws + L->mid_out);
   }
+  return SMLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
+                      smla_stream_t stream_handle) {
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  const int st = prepare_call(a, plan, &local, true, &p, &L);
+  if (st != SMLA_OK || a->T == 0) return st;
+  const int S = plan->num_splits;
+
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
+  if (p.validate && smla::launch_clear_error(p.err, stream) != hipSuccess)
+    return SMLA_ERR_HIP;
   if (smla::launch_decode(p, a->q_dtype, a->kv_dtype, stream) != hipSuccess)
     return SMLA_ERR_HIP;
   if (S > 1) {
@@ -249,6 +271,22 @@ int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
     c.stride = S;
     if (smla::launch_combine(c, stream) != hipSuccess) return SMLA_ERR_HIP;
   }
+  return SMLA_OK;
+}
+
+int sparse_mla_gather_only(const smla_decode_args* a, const smla_plan* plan,
+                           smla_stream_t stream_handle) {
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  const int st = prepare_call(a, plan, &local, false, &p, &L);
+  if (st != SMLA_OK || a->T == 0) return st;
+  if (a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
+  if (a->q_dtype != SMLA_DTYPE_BF16 || a->kv_dtype != SMLA_DTYPE_BF16)
+    return SMLA_ERR_UNSUPPORTED_DTYPE;
+  if (smla::launch_gather_only(p, reinterpret_cast<hipStream_t>(stream_handle)) !=
+      hipSuccess)
+    return SMLA_ERR_HIP;
   return SMLA_OK;
 }
 

@@ -50,6 +50,8 @@ struct CombineParams {
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// The H=128 BF16 gather without arithmetic or output (measurement aid).
+hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
 
 }  // namespace smla

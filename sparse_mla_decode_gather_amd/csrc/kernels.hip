@@ -660,7 +660,9 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-template <bool Q_FP8, bool SPLIT>
+// GATHER_ONLY: the same compaction and row gather with no arithmetic and no
+// output (a measurement aid: the attainable gather rate on the same tables).
+template <bool Q_FP8, bool SPLIT, bool GATHER_ONLY = false>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
   constexpr int NW = 4, H = 128, NT = 256;
@@ -714,7 +716,7 @@ void decode_hd_kernel(DecodeParams p) {
   __builtin_amdgcn_sched_barrier(0);
 
   bf16x8 qf[32];
-  {
+  if constexpr (!GATHER_ONLY) {
     const size_t qrow = ((size_t)t * H + head) * kD;
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) {
@@ -966,6 +968,16 @@ void decode_hd_kernel(DecodeParams p) {
       fetch_rows(min(2, ntiles - 1), rows);
       // The RPW rows of tile it+2 go out during the S^T MFMAs of tile it.
       auto qk_tile = [&](int it, bool do_issue) -> f32x16 {
+        if constexpr (GATHER_ONLY) {
+          f32x16 none;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) none[i] = -INFINITY;
+          if (do_issue) {
+#pragma unroll
+            for (int jj = 0; jj < RPW; ++jj) issue_row(it + 2, jj, rows[jj]);
+          }
+          return none;
+        }
         f32x16 sv = qk(stage(it), [&](int kk) {
           if (do_issue && (kk & 3) == 3) issue_row(it + 2, kk >> 2, rows[kk >> 2]);
         });
@@ -986,7 +998,9 @@ void decode_hd_kernel(DecodeParams p) {
       {
         const bool di = 2 < ntiles;
         bf16x8 pfr[NHB], vfr[kVLead];
-        step_block(BoolC<false>{}, kv_lds, p_lds, pfr, vfr, qk_tile(0, di), p_lds, no_hook);
+        const f32x16 sv0 = qk_tile(0, di);
+        if constexpr (!GATHER_ONLY)
+          step_block(BoolC<false>{}, kv_lds, p_lds, pfr, vfr, sv0, p_lds, no_hook);
         if (di) fetch_rows(min(3, ntiles - 1), rows);
       }
       for (int it = 1; it <= ntiles; ++it) {
@@ -995,7 +1009,7 @@ void decode_hd_kernel(DecodeParams p) {
         const bool di = it + 2 < ntiles;
         const u32x4* pr = p_lds + ((it - 1) & 1) * kPBuf;
         bf16x8 pfr[NHB], vfr[kVLead];
-        pv_prefetch(stage(it - 1), pr, pfr, vfr);
+        if constexpr (!GATHER_ONLY) pv_prefetch(stage(it - 1), pr, pfr, vfr);
         f32x16 sv;
         if (it < ntiles) {
           sv = qk_tile(it, di);
@@ -1003,8 +1017,9 @@ void decode_hd_kernel(DecodeParams p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
         }
-        step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
-                   p_lds + (it & 1) * kPBuf, no_hook);
+        if constexpr (!GATHER_ONLY)
+          step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
+                     p_lds + (it & 1) * kPBuf, no_hook);
         if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
       }
     }
@@ -1027,6 +1042,7 @@ void decode_hd_kernel(DecodeParams p) {
         for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
   }
   } while (again);
+  if constexpr (GATHER_ONLY) return;
 
   // ---- epilogue: the head owner finishes its head's normaliser ------------
   {
@@ -1177,6 +1193,13 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
   if (!kf) return launch_decode_hd<false>(p, stream);   // Q FP8 needs FP8 rows
   if (qf) return launch_decode_t<4, true, true>(p, stream);
   return launch_decode_t<4, false, true>(p, stream);
+}
+
+hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream) {
+  if (p.H != 128) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_hd_kernel<false, false, true>), dim3((unsigned)(p.T * p.S)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {

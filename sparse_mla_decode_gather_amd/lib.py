@@ -95,6 +95,9 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_decode.argtypes = [ctypes.POINTER(DecodeArgs),
                                       ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_decode.restype = ctypes.c_int
+    lib.sparse_mla_gather_only.argtypes = [ctypes.POINTER(DecodeArgs),
+                                           ctypes.POINTER(Plan), ctypes.c_void_p]
+    lib.sparse_mla_gather_only.restype = ctypes.c_int
     lib.sparse_mla_combine.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_float,
@@ -241,6 +244,21 @@ def decode(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
                      lse_scale=lse_scale, workspace=workspace, flags=flags)
     _check(load().sparse_mla_decode(ctypes.byref(args), ctypes.byref(plan),
                                     _stream(stream)), "sparse_mla_decode")
+    return plan
+
+
+def gather_only(q, swa_pool, compressed_pool, indices, *, topk_lens=None,
+                plan: Optional[Plan] = None, stream=None) -> Plan:
+    """sparse_mla_gather_only: the compaction and row gather of
+    sparse_mla_decode with no arithmetic and no output (measurement aid,
+    H = 128 BF16 only).  Returns the plan used."""
+    T, H, K = int(q.shape[0]), int(q.shape[1]), int(indices.shape[1])
+    if plan is None:
+        plan = plan_splits(T, H, K, dtype_code(q), dtype_code(swa_pool))
+    args = make_args(q, swa_pool, compressed_pool, indices, None,
+                     topk_lens=topk_lens)
+    _check(load().sparse_mla_gather_only(ctypes.byref(args), ctypes.byref(plan),
+                                         _stream(stream)), "sparse_mla_gather_only")
     return plan
 
 

@@ -30,6 +30,7 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {
         "sparse_mla_plan_splits", "sparse_mla_workspace_size",
         "sparse_mla_workspace_layout", "sparse_mla_decode",
+        "sparse_mla_gather_only",
         "sparse_mla_combine", "sparse_mla_get_device_error",
         "sparse_mla_status_string"}
     for n in names:
@@ -225,3 +226,39 @@ def test_combine_rejects_null_and_misaligned(so):
 
 def test_get_device_error_rejects_null(so):
     assert so.sparse_mla_get_device_error(None, None, None, None, None) == 1
+
+
+# ---------------------------------------------------------------------------
+# sparse_mla_gather_only: decode's checks, no outputs, H=128 BF16 only
+# ---------------------------------------------------------------------------
+
+def call_gather(so, a, p=None):
+    if p is None:
+        p = plan(max(a.T, 1), a.H if a.H in (64, 128) else 128, max(a.K, 1))
+    return so.sparse_mla_gather_only(ctypes.byref(a), ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("T", -1, 1), ("K", 0, 1), ("H", 96, 3), ("q", None, 1), ("indices", None, 1),
+    ("compressed_pool", None, 1), ("q", DUMMY + 8, 5), ("indices", DUMMY + 2, 5),
+    ("pool_row_stride", 500, 1), ("index_row_stride", 100, 1),
+    ("H", 64, 3), ("q_dtype", 1, 2), ("kv_dtype", 1, 2),
+])
+def test_gather_only_rejects(so, field, value, code):
+    a = good_args()
+    setattr(a, field, value)
+    if field == "q_dtype":
+        a.kv_dtype = 1        # FP8/FP8 is a valid decode pair, not a gather-only one
+    assert call_gather(so, a) == code
+
+
+def test_gather_only_needs_no_outputs_and_checks_the_plan(so):
+    assert so.sparse_mla_gather_only(None, None, None) == 1
+    a = good_args(T=0)
+    a.out = None
+    assert call_gather(so, a) == 0
+    a = good_args(T=4, K=2048)
+    a.out = a.workspace = None
+    p = plan(4, 128, 2048)
+    p.K = 1024
+    assert call_gather(so, a, p) == 6
