@@ -187,6 +187,14 @@ __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
       : "memory");
 }
 
+// 8 bytes of a row through a global (not flat) pointer: row addresses are
+// rebuilt from integers, and flat loads also count in lgkmcnt, which would
+// make every LDS wait of the tile loop wait for HBM too.
+typedef u32x2 __attribute__((address_space(1))) global_u32x2;
+__device__ __forceinline__ u32x2 load_global8(const uint8_t* row, uint32_t off) {
+  return *(const global_u32x2*)(row + off);
+}
+
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
                                              int c) {
   if (atomicCAS(err, 0, code) == 0) {
@@ -648,9 +656,12 @@ struct BoolC {
   static constexpr bool value = B;
 };
 
-// GATHER_ONLY: the same compaction and row gather with no arithmetic and no
-// output (a measurement aid: the attainable gather rate on the same tables).
-template <bool Q_FP8, bool SPLIT, bool GATHER_ONLY = false>
+// KV_FP8: E4M3FN rows go through registers (two tiles ahead, in two
+// register sets) and are widened to BF16 as they are written to LDS; BF16
+// rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
+// with no arithmetic and no output (a measurement aid: the attainable
+// gather rate on the same tables).
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
   constexpr int NW = 4, H = 128, NT = 256;
@@ -666,7 +677,7 @@ void decode_hd_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) u32x4 p_lds[2 * kPBuf];
   // code of each active row of the segment (SWA: row, compressed: row with
   // bit 31 set), padded with the last active row up to a whole tile
-  __shared__ __attribute__((aligned(16))) int32_t slots[kSegHd + kTile];
+  __shared__ __attribute__((aligned(16))) int32_t slots[kSegHd + 2 * kTile];
   __shared__ float inv_lds[H];
   __shared__ int32_t wave_cnt[NW];
   __shared__ int32_t restart_flag;
@@ -745,7 +756,7 @@ void decode_hd_kernel(DecodeParams p) {
   if (threadIdx.x == 0) restart_flag = 0;
   bool need_sticky = false;
 
-  constexpr int kLead = 4;
+  constexpr int kLead = KV_FP8 ? 3 : 4;
   auto qk = [&](const uint8_t* tb, auto&& every) -> f32x16 {
     bf16x8 a[kLead];
 #pragma unroll
@@ -896,8 +907,11 @@ void decode_hd_kernel(DecodeParams p) {
         slots[pos++] = last;
       }
     }
-    // the owner of the last active slot pads the tail of the last tile
-    const int ntiles = (n_act + kTile - 1) / kTile;
+    // The owner of the last active slot pads the tail of the last tile and,
+    // for FP8 rows, one more tile when the count is odd (its rows are all
+    // masked; an even count lets the two register sets alternate statically).
+    const int ntiles = KV_FP8 ? ((n_act + 2 * kTile - 1) / (2 * kTile)) * 2
+                              : (n_act + kTile - 1) / kTile;
     if (cnt > 0 && pos == n_act) {
       for (int i = n_act; i < ntiles * kTile; ++i) slots[i] = last;
     }
@@ -943,9 +957,88 @@ void decode_hd_kernel(DecodeParams p) {
     // Q has landed before the first row gather goes out: the compiler's own
     // waits for Q count only its loads, so they would otherwise also wait
     // for the gathers issued after Q.
-    if (ntiles > 0) wait_vmcnt<0>();
+    if (!KV_FP8 && ntiles > 0) wait_vmcnt<0>();
 
-    if (ntiles > 0) {
+    if constexpr (KV_FP8) {
+      if (ntiles > 0) {
+        // FP8 rows: each lane loads 8 bytes of each of the wave's 8 rows of
+        // tile it+2 during the S^T MFMAs of tile it, into the register set
+        // of that tile's parity; at the end of iteration it the rows of
+        // tile it+1 are widened and written to LDS.  These are ordinary
+        // loads, so the compiler's own waits are exact.
+        u32x2 rs0[RPW], rs1[RPW];
+        const uint8_t* rows[RPW];
+        const uint32_t lane_off8 = (uint32_t)lane * 8u;
+        auto load_set = [&](u32x2 (&rs)[RPW]) {
+#pragma unroll
+          for (int jj = 0; jj < RPW; ++jj) rs[jj] = load_global8(rows[jj], lane_off8);
+        };
+        auto store_set = [&](int tile, const u32x2 (&rs)[RPW]) {
+          uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes + wave_u * RPW * kRowPitch +
+                         lane * 16;
+#pragma unroll
+          for (int jj = 0; jj < RPW; ++jj)
+            *(u32x4*)(dst + jj * kRowPitch) = widen_e4m3fn_x8(rs[jj]);
+        };
+        fetch_rows(0, rows);
+        load_set(rs0);
+        fetch_rows(1, rows);
+        load_set(rs1);
+        fetch_rows(min(2, ntiles - 1), rows);
+        store_set(0, rs0);
+        // One iteration; PAR = it & 1 names the register set of tile it+2.
+        // QK: tile it exists; LOAD / STORE: load tile it+2, store tile it+1.
+        // All are compile-time so that the loop body has no branches and
+        // the compiler's load waits stay exact (at a branch merge it would
+        // wait for every load).  Loads past the last tile re-read valid
+        // rows (fetch_rows clamps), which hit in L2.
+        auto iteration = [&](auto par, auto pv, auto qk_on, auto load_on, auto store_on,
+                             int it) {
+          constexpr bool kOdd = decltype(par)::value;
+          constexpr bool kQK = decltype(qk_on)::value;
+          constexpr bool kLoad = decltype(load_on)::value;
+          constexpr bool kStore = decltype(store_on)::value;
+          u32x2 (&rs_next)[RPW] = kOdd ? rs1 : rs0;    // tile it+2
+          u32x2 (&rs_land)[RPW] = kOdd ? rs0 : rs1;    // tile it+1
+          // tile it is in LDS, P^T of tile it-1 is written, and the readers
+          // of the previous iteration are done
+          __syncthreads();
+          const u32x4* pr = p_lds + ((it + 1) & 1) * kPBuf;      // tile it-1
+          const uint8_t* vt = kv_lds + ((it + NSTAGE - 1) % NSTAGE) * kTileBytes;
+          f32x16 sv;
+          if constexpr (kQK) {
+            sv = qk(stage(it), [&](int kk) {
+              if (kLoad && (kk & 3) == 3)
+                rs_next[kk >> 2] = load_global8(rows[kk >> 2], lane_off8);
+            });
+            mfma_qk_drain(sv);
+            mask_tail(sv, it);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
+          }
+          // (the O^T operands are read after the S^T MFMAs here: the two
+          // register sets leave no room to hold them across S^T)
+          bf16x8 pfr[NHB], vfr[kVLead];
+          if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
+          step_block(pv, vt, pr, pfr, vfr, sv, p_lds + (it & 1) * kPBuf, no_hook);
+          if constexpr (kStore) store_set(it + 1, rs_land);
+          if constexpr (kLoad) fetch_rows(min(it + 3, ntiles - 1), rows);
+        };
+        using T_ = BoolC<true>;
+        using F_ = BoolC<false>;
+        iteration(F_{}, F_{}, T_{}, T_{}, T_{}, 0);
+        // ntiles is even: pairs of iterations with every step, then the last
+        // tile's iteration (nothing left to load or store) and the drain
+        int it = 1;
+        for (; it + 1 < ntiles; it += 2) {
+          iteration(T_{}, T_{}, T_{}, T_{}, T_{}, it);
+          iteration(F_{}, T_{}, T_{}, T_{}, T_{}, it + 1);
+        }
+        iteration(T_{}, T_{}, T_{}, F_{}, F_{}, ntiles - 1);
+        iteration(F_{}, T_{}, F_{}, F_{}, F_{}, ntiles);
+      }
+    } else if (ntiles > 0) {
       // LDS-DMA gather, two tiles ahead.
       const uint8_t* rows[RPW];
       for (int tl = 0; tl < min(2, ntiles); ++tl) {
@@ -1146,13 +1239,13 @@ __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
 
-template <bool QF>
+template <bool QF, bool KF>
 hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   if (p.S > 1)
-    hipLaunchKernelGGL((decode_hd_kernel<QF, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_hd_kernel<QF, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1178,14 +1271,14 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
     if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
     return launch_decode_t<2, false, true>(p, stream);
   }
-  if (!kf) return launch_decode_hd<false>(p, stream);   // Q FP8 needs FP8 rows
-  if (qf) return launch_decode_t<4, true, true>(p, stream);
-  return launch_decode_t<4, false, true>(p, stream);
+  if (!kf) return launch_decode_hd<false, false>(p, stream);   // Q FP8 needs FP8 rows
+  if (qf) return launch_decode_hd<true, true>(p, stream);
+  return launch_decode_hd<false, true>(p, stream);
 }
 
 hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream) {
   if (p.H != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_hd_kernel<false, false, true>), dim3((unsigned)(p.T * p.S)),
+  hipLaunchKernelGGL((decode_hd_kernel<false, false, false, true>), dim3((unsigned)(p.T * p.S)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
