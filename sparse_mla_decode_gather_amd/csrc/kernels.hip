@@ -662,8 +662,7 @@ struct BoolC {
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false>
-__global__ __launch_bounds__(256, 1)
-void decode_hd_kernel(DecodeParams p) {
+__device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   constexpr int NW = 4, H = 128, NT = 256;
   constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
   // LDS tiles: i-1 (read by O^T), i (S^T), i+1 and i+2 (landing).
@@ -1192,6 +1191,18 @@ void decode_hd_kernel(DecodeParams p) {
   }
 }
 
+template <bool Q_FP8, bool KV_FP8, bool SPLIT>
+__global__ __launch_bounds__(256, 1)
+void decode_hd_kernel(DecodeParams p) {
+  decode_hd_body<Q_FP8, KV_FP8, SPLIT>(p);
+}
+
+// The row gather of decode_hd_kernel alone (BF16 rows), under its own name.
+__global__ __launch_bounds__(256, 1)
+void gather_only_kernel(DecodeParams p) {
+  decode_hd_body<false, false, false, true>(p);
+}
+
 // ---------------------------------------------------------------------------
 // combine kernel: one wave per (token, head); lane owns 8 output dims
 // ---------------------------------------------------------------------------
@@ -1278,7 +1289,7 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
 
 hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream) {
   if (p.H != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_hd_kernel<false, false, false, true>), dim3((unsigned)(p.T * p.S)),
+  hipLaunchKernelGGL(gather_only_kernel, dim3((unsigned)(p.T * p.S)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -3,8 +3,12 @@
     python -m sparse_mla_decode_gather_amd.rocprof_summary stats <dir> <cmd>
     python -m sparse_mla_decode_gather_amd.rocprof_summary traffic \\
         <fetch_dir> <write_dir> <copy_bytes> <cmd>
+    python -m sparse_mla_decode_gather_amd.rocprof_summary sq <cmd> <dir>...
 
 ``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv).
+``sq`` gives the median per dispatch of every counter in one or more
+--pmc runs over the decode kernels, with the MFMA-busy and waiting
+fractions derived from them.
 ``traffic`` turns a FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch)
 into HBM bytes per decode launch, calibrated by the same counters on a
 plain device copy of known size taken in the same process: the factor is
@@ -23,7 +27,7 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-DECODE = "decode_kernel"
+DECODE = ("decode_kernel", "decode_hd_kernel")   # the decode kernels (not gather_only)
 COPY_PATTERNS = ("copy", "Copy")
 
 
@@ -49,7 +53,7 @@ def stats(directory: str, cmd: str) -> str:
              "kernel | calls | average_ns | min_ns | max_ns | percent"]
     for r in rows:
         name = r["Name"]
-        if DECODE in name or "combine_kernel" in name:
+        if any(d in name for d in DECODE) or "combine_kernel" in name:
             short = name.replace("smla::(anonymous namespace)::", "")
             short = short.replace("void ", "").split("(smla::")[0]
             lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
@@ -68,8 +72,8 @@ def _per_dispatch(rows, counter, pattern_ok):
 
 
 def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cmd: str) -> str:
-    is_decode = lambda n: DECODE in n
-    is_copy = lambda n: any(p in n for p in COPY_PATTERNS) and DECODE not in n
+    is_decode = lambda n: any(d in n for d in DECODE)
+    is_copy = lambda n: any(p in n for p in COPY_PATTERNS) and not is_decode(n)
     f_rows = _csv(fetch_dir, "counter_collection.csv")
     w_rows = _csv(write_dir, "counter_collection.csv")
     fd = _per_dispatch(f_rows, "FETCH_SIZE", is_decode)
@@ -103,6 +107,29 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cmd: str) -> str:
     ]) + "\n"
 
 
+def sq(dirs, cmd: str, simds: int = 1024, xcds: int = 8) -> str:
+    is_decode = lambda n: any(d in n for d in DECODE)
+    med = {}
+    for d in dirs:
+        rows = _csv(d, "counter_collection.csv")
+        for name in sorted({r["Counter_Name"] for r in rows}):
+            vals = _per_dispatch(rows, name, is_decode)
+            if vals:
+                med[name] = statistics.median(vals)
+    lines = ["# SQ counters of the decode kernel (median per dispatch; summed over the chip)",
+             f"# command: {cmd}"]
+    lines += [f"{k}: {v:.4g}" for k, v in sorted(med.items())]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in med and "GRBM_GUI_ACTIVE" in med:
+        # GRBM_GUI_ACTIVE is summed over the XCDs; SQ_VALU_MFMA_BUSY_CYCLES
+        # over all SIMDs
+        busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (med["GRBM_GUI_ACTIVE"] / xcds * simds)
+        lines.append(f"# derived: MFMA busy fraction of SIMD cycles = {busy:.3f}")
+    if "SQ_WAIT_ANY" in med and "SQ_WAVE_CYCLES" in med:
+        lines.append("# derived: wave-time waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES) = "
+                     f"{med['SQ_WAIT_ANY'] / med['SQ_WAVE_CYCLES']:.3f}")
+    return "\n".join(lines) + "\n"
+
+
 if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
@@ -110,5 +137,7 @@ if __name__ == "__main__":
     elif mode == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5]),
               end="")
+    elif mode == "sq":
+        print(sq(sys.argv[3:], sys.argv[2]), end="")
     else:
         raise SystemExit(__doc__)
