@@ -1214,9 +1214,22 @@ void combine_kernel(CombineParams p) {
   if (item >= p.T * p.H) return;
   const int h = item % p.H;
   const float* ml = p.mid_lse + (size_t)item * p.stride;
+  const uint16_t* base = p.mid_out + (size_t)item * p.stride * kD + lane * 8;
+  // Every load goes out before any result is used, so the memory latencies
+  // of the LSEs, the sink and the first kFirst partial rows overlap.  An
+  // empty split's weight is 0 (its partial row is 0 too), so it is read and
+  // added like any other.
+  constexpr int kFirst = 16, kBatch = 8;
   const float mine = (lane < p.S) ? ml[lane] : -INFINITY;
+  // (loaded without a branch; with no sinks the value read is unused)
+  const float sink = *(p.sinks ? p.sinks + h : ml);
+  u32x4 v[kFirst];
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j)
+    if (j < p.S) v[j] = *(const u32x4*)(base + (size_t)j * kD);
+
   float L = wave_max(mine);
-  const float sl = p.sinks ? p.sinks[h] * kLog2e : -INFINITY;
+  const float sl = p.sinks ? sink * kLog2e : -INFINITY;
   L = fmaxf(L, sl);
   float w = 0.f;
   if (lane < p.S && mine != -INFINITY) w = fast_exp2(mine - L);
@@ -1226,16 +1239,24 @@ void combine_kernel(CombineParams p) {
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  const uint16_t* base = p.mid_out + (size_t)item * p.stride * kD + lane * 8;
-  for (int s = 0; s < p.S; ++s) {
-    const float ws = __shfl(w, s);
-    if (ws == 0.f) continue;   // uniform across the wave
-    const u32x4 v = *(const u32x4*)(base + (size_t)s * kD);
+  auto add = [&](const u32x4& row, float ws) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[2 * i] += ws * __uint_as_float(v[i] << 16);
-      acc[2 * i + 1] += ws * __uint_as_float(v[i] & 0xFFFF0000u);
+      acc[2 * i] += ws * __uint_as_float(row[i] << 16);
+      acc[2 * i + 1] += ws * __uint_as_float(row[i] & 0xFFFF0000u);
     }
+  };
+#pragma unroll
+  for (int j = 0; j < kFirst; ++j)
+    if (j < p.S) add(v[j], __shfl(w, j));
+  for (int s0 = kFirst; s0 < p.S; s0 += kBatch) {
+    u32x4 vb[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j < p.S) vb[j] = *(const u32x4*)(base + (size_t)(s0 + j) * kD);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      if (s0 + j < p.S) add(vb[j], __shfl(w, s0 + j));
   }
   const float inv = (W > 0.f) ? 1.f / W : 0.f;
   u32x4 r;
