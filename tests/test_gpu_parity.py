@@ -250,6 +250,48 @@ def test_wide_table_multiple_segments():
     check(w, what="K=5000 S=3", plan=L.plan_splits(T, 128, K, num_splits=3))
 
 
+@pytest.mark.parametrize("q", [W.BF16, W.FP8])
+def test_fp8_rows_at_h128_edges_segments_and_restarts(q):
+    """FP8 rows at H=128 take the register-staged path of the H=128 kernel
+    (two register sets, an extra all-masked tile when the tile count is
+    odd).  Ragged and tiny lengths give odd, single and empty tile counts;
+    K=5000 crosses segments; wide logits force restarts."""
+    need_gpu()
+    qc = L.DTYPE_FP8_E4M3FN if q == W.FP8 else L.DTYPE_BF16
+    kc = L.DTYPE_FP8_E4M3FN
+    rng = np.random.default_rng(21)
+    T, K = 12, 700
+    idx = np.concatenate([rng.integers(0, 600, (T, 128)),
+                          rng.integers(0, 900, (T, K - 128))], 1).astype(np.int32)
+    idx[3, :] = -1
+    idx[5, ::3] = -1
+    idx[6, 200:230] = idx[6, 300]          # duplicates count per slot
+    lens = [0, 1, 31, 32, 33, 127, 128, 129, 700, 650, 64, 97]
+    w = custom(idx, lens=lens, H=128, kv=W.FP8, q=q)
+    check(w, what=f"fp8 rows H=128 q={q} edges")
+    check(w, plan=L.plan_splits(T, 128, K, qc, kc, num_splits=5),
+          what=f"fp8 rows H=128 q={q} edges S=5")
+
+    T, K = 3, 5000
+    idx = np.concatenate([rng.integers(0, 600, (T, 128)),
+                          rng.integers(0, 20000, (T, K - 128))], 1).astype(np.int32)
+    idx[1, 4000:] = -1
+    w = custom(idx, lens=[5000, 4500, 2100], comp_rows=20000, H=128, kv=W.FP8, q=q)
+    check(w, what=f"fp8 rows H=128 q={q} K=5000",
+          plan=L.plan_splits(T, 128, K, qc, kc, num_splits=1))
+
+    idx = np.concatenate([rng.integers(0, 600, (4, 128)),
+                          rng.integers(0, 900, (4, 1400))], 1).astype(np.int32)
+    # FP8 q holds x/0.05, so its bmm1 carries the 0.05 (as the workloads
+    # fold it) and the logit spread - hence the restarts - matches the BF16
+    # case; unscaled, the LSE would sit near 5e4, where one fp32 ulp already
+    # exceeds the 1e-3 LSE bar.
+    w = custom(idx, lens=[1528, 900, 200, 1528], H=128, kv=W.FP8, q=q,
+               b1=2.0 * (0.05 if q == W.FP8 else 1.0))
+    check(w, what=f"fp8 rows H=128 q={q} wide logits",
+          plan=L.plan_splits(4, 128, 1528, qc, kc, num_splits=1))
+
+
 def test_padded_pool_rows():
     need_gpu()
     rng = np.random.default_rng(4)
