@@ -22,13 +22,16 @@ docstring says "parity unpinned".
 
 from .formats import bf16_bits_to_f64, e4m3fn_bits_to_f64, decode_bits, \
     round_to_bf16
-from .sparse_mla import (SWA_COLUMNS, active_slots, decode_token,
-                         sparse_mla_decode, split_partials, combine,
+from .sparse_mla import (SWA_COLUMNS, active_slots, active_slots_segments,
+                         decode_token, sparse_mla_decode,
+                         sparse_mla_decode_segments, split_partials, combine,
                          split_columns)
-from .brute import brute_force_decode
+from .brute import brute_force_decode, brute_force_decode_segments
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "decode_bits", "round_to_bf16",
-    "SWA_COLUMNS", "active_slots", "decode_token", "sparse_mla_decode",
-    "split_partials", "combine", "split_columns", "brute_force_decode",
+    "SWA_COLUMNS", "active_slots", "active_slots_segments", "decode_token",
+    "sparse_mla_decode", "sparse_mla_decode_segments", "split_partials",
+    "combine", "split_columns", "brute_force_decode",
+    "brute_force_decode_segments",
 ]

@@ -28,28 +28,69 @@ from .formats import decode_bits
 _SWA = 128
 
 
+def _combined_multiset(indices, topk_lens, t):
+    """Multiset of (pool, row) named by token t's active slots of a combined
+    table (columns < 128 name SWA rows)."""
+    K = indices.shape[1]
+    n = K if topk_lens is None else int(topk_lens[t])
+    mult = Counter()
+    for c in range(K):
+        if c >= n:
+            break
+        r = int(indices[t][c])
+        if r != -1:
+            mult[(0 if c < _SWA else 1, r)] += 1
+    return mult
+
+
+def _segments_multiset(swa_indices, swa_lens, extra_indices, extra_lens, t):
+    """Multiset of (pool, row) named by token t's active slots of an SWA
+    table and an extra (compressed) table, each with its own length."""
+    mult = Counter()
+    for pool, tab, lens in ((0, swa_indices, swa_lens), (1, extra_indices, extra_lens)):
+        if tab is None:
+            continue
+        n = tab.shape[1] if lens is None else int(lens[t])
+        for c in range(min(n, tab.shape[1])):
+            r = int(tab[t][c])
+            if r != -1:
+                mult[(pool, r)] += 1
+    return mult
+
+
 def brute_force_decode(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
                        indices, topk_lens, sinks, bmm1_scale, bmm2_scale,
                        lse_scale, dps: int = 50):
     """Returns (out [T,H,D] float64, lse [T,H] float64)."""
+    return _brute(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                  lambda t: _combined_multiset(indices, topk_lens, t),
+                  sinks, bmm1_scale, bmm2_scale, lse_scale, dps)
+
+
+def brute_force_decode_segments(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                                swa_indices, extra_indices, swa_lens, extra_lens,
+                                sinks, bmm1_scale, bmm2_scale, lse_scale,
+                                dps: int = 50):
+    """The two-segment form (SWA table + extra compressed table, one length
+    each) by the same multiset evaluation.  Returns (out, lse)."""
+    return _brute(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                  lambda t: _segments_multiset(swa_indices, swa_lens,
+                                               extra_indices, extra_lens, t),
+                  sinks, bmm1_scale, bmm2_scale, lse_scale, dps)
+
+
+def _brute(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype, multiset_of,
+           sinks, bmm1_scale, bmm2_scale, lse_scale, dps):
     b1 = mpmath.mpf(float(np.float32(bmm1_scale)))
     b2 = mpmath.mpf(float(np.float32(bmm2_scale)))
     g = mpmath.mpf(float(np.float32(lse_scale)))
     T, H, D = q_bits.shape
-    K = indices.shape[1]
     q = decode_bits(q_bits, q_dtype)
     out = np.zeros((T, H, D))
     lse = np.zeros((T, H))
     with mpmath.workdps(dps):
         for t in range(T):
-            n = K if topk_lens is None else int(topk_lens[t])
-            mult = Counter()
-            for c in range(K):
-                if c >= n:
-                    break
-                r = int(indices[t][c])
-                if r != -1:
-                    mult[(0 if c < _SWA else 1, r)] += 1
+            mult = multiset_of(t)
             rows = {}
             for (pool, r) in mult:
                 src = swa_bits if pool == 0 else comp_bits

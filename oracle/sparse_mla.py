@@ -39,7 +39,12 @@ carries no value row; ``out_lse`` includes the sink term; an empty A_t gives
 out = 0 and lse = -inf (or the sink's own term); duplicate indices count once
 per slot; ``seq_lens`` does not change the result.
 
-Parity status: pinned (tests/test_oracle_pins.py) by an independent
+Two-segment form (``sparse_mla_decode_segments``): the same definition
+with A_t = the active slots of an SWA table (length swa_topk_lens[t]) and of
+an extra compressed table (length extra_topk_lens[t]) together.
+
+Parity status: pinned (tests/test_oracle_pins.py, and for the two-segment
+form tests/test_oracle_segments.py) by an independent
 multiset brute force in arbitrary precision, closed forms, invariants and
 torch's float64 scaled_dot_product_attention, except that "out_lse includes
 the sink" is a reading the pages do not settle (parity unpinned for that
@@ -75,6 +80,35 @@ def active_slots(idx_row: np.ndarray, topk_len: Optional[int]):
         if r == -1:
             continue
         out.append((c, 0 if c < SWA_COLUMNS else 1, r))
+    return out
+
+
+def active_slots_segments(swa_row, swa_len: Optional[int], extra_row,
+                          extra_len: Optional[int]):
+    """Active slots of one token in the two-segment form, as
+    (column, pool, row): FlashInfer ``trtllm_batch_decode_sparse_mla_dsv4``
+    (introduction, packed-backend paragraph, and parameters
+    ``swa_topk_lens``, ``extra_sparse_indices``, ``extra_sparse_topk_lens``)
+    and the Cake page (``indices``/``topk_length`` with
+    ``extra_indices``/``extra_topk_length``): the SWA table and its length
+    describe the SWA segment, the extra table and its length the compressed
+    segment, and the softmax runs over both.  SWA slot c keeps column c;
+    extra slot j gets column K1 + j (K1 = the SWA table's width), so the
+    split form cuts one row of K1 + K2 columns.  A length counts its own
+    table only (None = the whole table); -1 masks a slot in either table."""
+    K1 = 0 if swa_row is None else int(np.asarray(swa_row).shape[0])
+    K2 = 0 if extra_row is None else int(np.asarray(extra_row).shape[0])
+    n1 = K1 if swa_len is None else int(swa_len)
+    n2 = K2 if extra_len is None else int(extra_len)
+    out = []
+    for c in range(min(n1, K1)):
+        r = int(swa_row[c])
+        if r != -1:
+            out.append((c, 0, r))
+    for j in range(min(n2, K2)):
+        r = int(extra_row[j])
+        if r != -1:
+            out.append((K1 + j, 1, r))
     return out
 
 
@@ -138,6 +172,39 @@ def sparse_mla_decode(q_bits, q_dtype: str, swa_bits, comp_bits, kv_dtype: str,
     for t in tokens:
         ln = None if topk_lens is None else int(topk_lens[t])
         slots = active_slots(np.asarray(indices[t]), ln)
+        rows = gather_rows(slots, swa_bits, comp_bits, kv_dtype)
+        q_t = decode_bits(q_bits[t], q_dtype)
+        o, l, lns = decode_token(q_t, rows, sk, b1, b2, g)
+        outs.append(o)
+        lses.append(l)
+        lses_ns.append(lns)
+        nact.append(len(slots))
+    return {"out": np.stack(outs), "lse": np.stack(lses),
+            "lse_nosink": np.stack(lses_ns), "n_active": np.array(nact)}
+
+
+def sparse_mla_decode_segments(q_bits, q_dtype: str, swa_bits, comp_bits,
+                               kv_dtype: str, swa_indices, extra_indices,
+                               swa_topk_lens=None, extra_topk_lens=None,
+                               sinks=None, bmm1_scale: float = 1.0,
+                               bmm2_scale: float = 1.0, lse_scale: float = 1.0,
+                               tokens: Optional[Sequence[int]] = None):
+    """The two-segment form (see ``active_slots_segments``): swa_indices
+    [T,K1] into the SWA pool with swa_topk_lens [T], extra_indices [T,K2]
+    into the compressed pool with extra_topk_lens [T]; either table may be
+    None (width 0).  Everything after the selection is ``decode_token``.
+    Returns the same dict as ``sparse_mla_decode``."""
+    T = q_bits.shape[0]
+    tokens = range(T) if tokens is None else list(tokens)
+    b1, b2, g = _fp32(bmm1_scale), _fp32(bmm2_scale), _fp32(lse_scale)
+    sk = None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64)
+    outs, lses, lses_ns, nact = [], [], [], []
+    for t in tokens:
+        slots = active_slots_segments(
+            None if swa_indices is None else np.asarray(swa_indices[t]),
+            None if swa_topk_lens is None else int(swa_topk_lens[t]),
+            None if extra_indices is None else np.asarray(extra_indices[t]),
+            None if extra_topk_lens is None else int(extra_topk_lens[t]))
         rows = gather_rows(slots, swa_bits, comp_bits, kv_dtype)
         q_t = decode_bits(q_bits[t], q_dtype)
         o, l, lns = decode_token(q_t, rows, sk, b1, b2, g)
