@@ -180,6 +180,49 @@ int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
 int sparse_mla_decode(const smla_decode_args* args, const smla_plan* plan,
                       smla_stream_t stream);
 
+/* The two-segment form of the token tables (FlashInfer
+ * "trtllm_batch_decode_sparse_mla_dsv4", introduction (packed-backend
+ * paragraph) and parameters "swa_topk_lens", "extra_sparse_indices",
+ * "extra_sparse_topk_lens"; FlashInfer "cake_sparse_mla_sm120_dsv4_nvfp4_decode",
+ * parameters "indices"/"topk_length" and "extra_indices"/"extra_topk_length"):
+ * token t's SWA rows are named by an SWA table with its own active length,
+ * its compressed rows by an extra table with its own length, and the
+ * softmax runs over the active slots of both.  -1 masks a slot in either
+ * table; columns at or past a table's length are never read as rows.
+ * Device pointers; the caller owns them. */
+typedef struct smla_segments {
+  const int32_t* swa_indices;     /* [T, swa_row_stride] rows of swa_pool; NULL iff
+                                     swa_width == 0 */
+  int64_t swa_row_stride;         /* elements; 0 means swa_width */
+  const int32_t* swa_topk_lens;   /* [T] active SWA columns in [0, swa_width], or
+                                     NULL = swa_width */
+  const int32_t* extra_indices;   /* [T, extra_row_stride] rows of compressed_pool;
+                                     NULL iff extra_width == 0 */
+  int64_t extra_row_stride;       /* elements; 0 means extra_width */
+  const int32_t* extra_topk_lens; /* [T] active extra columns in [0, extra_width],
+                                     or NULL = extra_width */
+  int32_t swa_width;              /* >= 0 */
+  int32_t extra_width;            /* >= 0; swa_width + extra_width == args->K */
+} smla_segments;
+
+/* sparse_mla_decode with the tables in two segments.  args->K is the total
+ * width swa_width + extra_width: the split plan and the split partials cut
+ * that row, SWA column c being column c and extra column j being column
+ * swa_width + j (also the column a validation error reports).
+ * args->indices and args->topk_lens must be NULL and args->index_row_stride
+ * is ignored; every other field, the plan, the workspace and the outputs
+ * are exactly as for sparse_mla_decode.  swa_pool is required when
+ * swa_width > 0, compressed_pool when extra_width > 0.  A length outside its
+ * range is clamped (and reported in validate mode as
+ * SMLA_DEVERR_TOPK_LEN).  Returns SMLA_ERR_INVALID_ARG for a NULL seg,
+ * widths that do not add up to K, a table missing for a non-zero width, a
+ * row stride below its width, or non-NULL args->indices / topk_lens;
+ * otherwise as sparse_mla_decode.  Asynchronous, no allocation, graph
+ * capturable. */
+int sparse_mla_decode_segments(const smla_decode_args* args,
+                               const smla_segments* seg, const smla_plan* plan,
+                               smla_stream_t stream);
+
 /* Measurement aid (not part of the method): run only the table compaction
  * and the row gather of sparse_mla_decode on the same arguments and plan,
  * with no arithmetic and no output, to give the attainable gathered-row

@@ -166,28 +166,53 @@ namespace {
 // Argument checks shared by sparse_mla_decode and sparse_mla_gather_only,
 // and the kernel parameters they resolve to.  *plan is replaced by
 // *local when the caller passed none.  Returns SMLA_OK or a status.
-int prepare_call(const smla_decode_args* a, const smla_plan*& plan, smla_plan* local,
+// seg == NULL: the combined table (args->indices, args->topk_lens); else the
+// two-segment form, where args->indices and args->topk_lens must be NULL.
+int prepare_call(const smla_decode_args* a, const smla_segments* seg,
+                 const smla_plan*& plan, smla_plan* local,
                  bool with_outputs, smla::DecodeParams* p, Layout* L) {
   if (!a) return SMLA_ERR_INVALID_ARG;
   if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
   if (a->H != 64 && a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (!dtype_pair_ok(a->q_dtype, a->kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
+  // the two tables: widths, rows, strides (in elements)
+  int k1, k2;
+  const int32_t *t1, *t2;
+  int64_t s1, s2;
+  if (seg) {
+    if (seg->swa_width < 0 || seg->extra_width < 0 ||
+        (int64_t)seg->swa_width + seg->extra_width != a->K)
+      return SMLA_ERR_INVALID_ARG;
+    if (a->indices || a->topk_lens) return SMLA_ERR_INVALID_ARG;
+    k1 = seg->swa_width;
+    k2 = seg->extra_width;
+    t1 = seg->swa_indices;
+    t2 = seg->extra_indices;
+    s1 = seg->swa_row_stride == 0 ? k1 : seg->swa_row_stride;
+    s2 = seg->extra_row_stride == 0 ? k2 : seg->extra_row_stride;
+  } else {
+    k1 = std::min(a->K, smla::kSwaColumns);
+    k2 = a->K - k1;
+    t1 = a->indices;
+    s1 = a->index_row_stride == 0 ? a->K : a->index_row_stride;
+    if (s1 < a->K) return SMLA_ERR_INVALID_ARG;
+    t2 = a->indices ? a->indices + k1 : nullptr;
+    s2 = s1;
+  }
   if (a->T == 0) return SMLA_OK;
-  if (!a->q || !a->swa_pool || !a->indices || (with_outputs && !a->out))
-    return SMLA_ERR_INVALID_ARG;
-  if (a->K > smla::kSwaColumns && !a->compressed_pool) return SMLA_ERR_INVALID_ARG;
+  if (!a->q || (with_outputs && !a->out)) return SMLA_ERR_INVALID_ARG;
+  if (k1 > 0 && (!t1 || !a->swa_pool || s1 < k1)) return SMLA_ERR_INVALID_ARG;
+  if (k2 > 0 && (!t2 || !a->compressed_pool || s2 < k2)) return SMLA_ERR_INVALID_ARG;
   if (a->swa_rows < 0 || a->compressed_rows < 0) return SMLA_ERR_INVALID_ARG;
   if ((int64_t)a->T * a->H > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
   const int64_t row_stride = a->pool_row_stride == 0 ? smla::kHeadDim : a->pool_row_stride;
   if (row_stride < smla::kHeadDim) return SMLA_ERR_INVALID_ARG;
-  const int64_t idx_stride = a->index_row_stride == 0 ? a->K : a->index_row_stride;
-  if (idx_stride < a->K) return SMLA_ERR_INVALID_ARG;
   if (a->cum_seq_lens_q && a->num_requests < 1) return SMLA_ERR_INVALID_ARG;
   const int kv_elem = a->kv_dtype == SMLA_DTYPE_FP8_E4M3FN ? 1 : 2;
   if (!aligned(a->q, 16) || (with_outputs && !aligned(a->out, 16)) ||
-      !aligned(a->swa_pool, 16) ||
+      (a->swa_pool && !aligned(a->swa_pool, 16)) ||
       (a->compressed_pool && !aligned(a->compressed_pool, 16)) ||
-      (row_stride * kv_elem) % 16 != 0 || !aligned(a->indices, 4))
+      (row_stride * kv_elem) % 16 != 0 || (t1 && !aligned(t1, 4)) || (t2 && !aligned(t2, 4)))
     return SMLA_ERR_MISALIGNED;
 
   if (!plan) {
@@ -213,12 +238,20 @@ int prepare_call(const smla_decode_args* a, const smla_plan*& plan, smla_plan* l
   p->q = a->q;
   p->swa = static_cast<const uint8_t*>(a->swa_pool);
   p->comp = static_cast<const uint8_t*>(a->compressed_pool);
-  p->swa_rows = a->swa_rows;
+  p->swa_rows = a->swa_pool ? a->swa_rows : 0;
   p->comp_rows = a->compressed_pool ? a->compressed_rows : 0;
   p->row_stride_bytes = row_stride * kv_elem;
-  p->indices = a->indices;
-  p->index_row_stride = idx_stride;
-  p->topk_lens = a->topk_lens;
+  // a table of width 0 is never read; point it at the other one so that
+  // every pointer the kernel forms is a real address
+  p->indices = k1 > 0 ? t1 : t2;
+  p->index_row_stride = k1 > 0 ? s1 : s2;
+  p->indices2 = k2 > 0 ? t2 : t1;
+  p->index_row_stride2 = k2 > 0 ? s2 : s1;
+  p->swa_cols = seg ? k1 : smla::kSwaColumns;
+  p->K2 = k2;
+  p->segmented = seg ? 1 : 0;
+  p->topk_lens = seg ? seg->swa_topk_lens : a->topk_lens;
+  p->lens2 = seg ? seg->extra_topk_lens : nullptr;
   p->sinks = a->sinks;
   p->scale_log2 = (float)((double)a->bmm1_scale * 1.4426950408889634);
   p->bmm2 = a->bmm2_scale;
@@ -239,20 +272,10 @@ int prepare_call(const smla_decode_args* a, const smla_plan*& plan, smla_plan* l
   return SMLA_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
-                      smla_stream_t stream_handle) {
-  smla_plan local;
-  smla::DecodeParams p;
-  Layout L;
-  const int st = prepare_call(a, plan, &local, true, &p, &L);
-  if (st != SMLA_OK || a->T == 0) return st;
+// The split kernel, then the combine when the plan splits.
+int launch_all(const smla_decode_args* a, const smla_plan* plan,
+               const smla::DecodeParams& p, hipStream_t stream) {
   const int S = plan->num_splits;
-
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
   if (p.validate && smla::launch_clear_error(p.err, stream) != hipSuccess)
     return SMLA_ERR_HIP;
   if (smla::launch_decode(p, a->q_dtype, a->kv_dtype, stream) != hipSuccess)
@@ -274,12 +297,37 @@ int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
   return SMLA_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
+                      smla_stream_t stream_handle) {
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  const int st = prepare_call(a, nullptr, plan, &local, true, &p, &L);
+  if (st != SMLA_OK || a->T == 0) return st;
+  return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
+}
+
+int sparse_mla_decode_segments(const smla_decode_args* a, const smla_segments* seg,
+                               const smla_plan* plan, smla_stream_t stream_handle) {
+  if (!seg) return SMLA_ERR_INVALID_ARG;
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  const int st = prepare_call(a, seg, plan, &local, true, &p, &L);
+  if (st != SMLA_OK || a->T == 0) return st;
+  return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
+}
+
 int sparse_mla_gather_only(const smla_decode_args* a, const smla_plan* plan,
                            smla_stream_t stream_handle) {
   smla_plan local;
   smla::DecodeParams p;
   Layout L;
-  const int st = prepare_call(a, plan, &local, false, &p, &L);
+  const int st = prepare_call(a, nullptr, plan, &local, false, &p, &L);
   if (st != SMLA_OK || a->T == 0) return st;
   if (a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (a->q_dtype != SMLA_DTYPE_BF16 || a->kv_dtype != SMLA_DTYPE_BF16)

@@ -35,6 +35,18 @@ struct DecodeParams {
   int32_t T, H, K, S;
   int32_t split_cols;            // columns per split
   int32_t validate;
+  // The token's columns [0, K) split in two tables: columns < swa_cols read
+  // `indices` (SWA pool), the others read `indices2` at column - swa_cols
+  // (compressed pool).  Combined form: indices2 = indices + 128 and
+  // topk_lens counts both; two-segment form (segmented = 1): topk_lens
+  // counts the first table's active columns and lens2 the second's.
+  const int32_t* indices2;
+  int64_t index_row_stride2;
+  const int32_t* lens2;          // [T] or null (= K2)
+  int32_t swa_cols;
+  int32_t K2;                    // width of the second table
+  int32_t segmented;
+  int32_t pad_;
 };
 
 struct CombineParams {

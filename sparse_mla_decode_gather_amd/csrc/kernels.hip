@@ -203,6 +203,53 @@ __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
   }
 }
 
+// A token's table as one row of columns [0, K): columns below P read the
+// first table and name SWA rows, the others read the second table (at column
+// c - P) and name compressed rows.  The combined form (FlashInfer
+// trtllm_batch_decode_sparse_mla_dsv4, "sparse_indices"/"sparse_topk_lens":
+// 128 SWA columns, one length counting both) and the two-segment form (same
+// page, "swa_topk_lens"/"extra_sparse_indices"/"extra_sparse_topk_lens";
+// the Cake page's "extra_indices"/"extra_topk_length": one length per
+// table) differ only in where the tables and lengths come from.
+struct TokenTable {
+  const int32_t* row1;
+  const int32_t* row2;
+  int P;        // columns of the first table
+  int L1, L2;   // active columns of each table
+  // the stored entry of column c (whether or not the column is active)
+  __device__ __forceinline__ int raw(int c) const { return c < P ? row1[c] : row2[c - P]; }
+  // column c is below its table's length
+  __device__ __forceinline__ bool live(int c) const { return c < P ? c < L1 : c - P < L2; }
+  // one past the last column that can be active
+  __device__ __forceinline__ int end() const { return L2 > 0 ? P + L2 : L1; }
+};
+
+__device__ __forceinline__ TokenTable token_table(const DecodeParams& p, int t) {
+  TokenTable tt;
+  tt.P = p.swa_cols;
+  tt.row1 = p.indices + (int64_t)t * p.index_row_stride;
+  tt.row2 = p.indices2 + (int64_t)t * p.index_row_stride2;
+  tt.L1 = tt.L2 = 0;
+  return tt;
+}
+
+// Reads the token's length(s) into tt (clamped to the tables) and reports
+// whether they were in range.
+__device__ __forceinline__ bool token_lengths(const DecodeParams& p, int t, TokenTable& tt) {
+  if (p.segmented) {
+    const int a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
+    const int b = p.lens2 ? p.lens2[t] : p.K2;
+    tt.L1 = min(max(a, 0), p.swa_cols);
+    tt.L2 = min(max(b, 0), p.K2);
+    return a >= 0 && a <= p.swa_cols && b >= 0 && b <= p.K2;
+  }
+  const int len = p.topk_lens ? p.topk_lens[t] : p.K;
+  const int l = min(max(len, 0), p.K);
+  tt.L1 = min(l, tt.P);
+  tt.L2 = max(l - tt.P, 0);
+  return len >= 0 && len <= p.K;
+}
+
 // ---------------------------------------------------------------------------
 // split kernel
 // ---------------------------------------------------------------------------
@@ -259,12 +306,11 @@ void decode_kernel(DecodeParams p) {
   const int s = item - t * p.S;
   const int head = wave * 32 + l32;
 
-  int len = p.topk_lens ? p.topk_lens[t] : p.K;
-  if (p.validate && threadIdx.x == 0 && s == 0 && (len < 0 || len > p.K))
-    record_error(p.err, 2, t, -1);
-  len = min(max(len, 0), p.K);
+  TokenTable tt = token_table(p, t);
+  const bool lens_ok = token_lengths(p, t, tt);
+  if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
   const int c_begin = s * p.split_cols;
-  const int c_end = min(len, c_begin + p.split_cols);
+  const int c_end = min(tt.end(), c_begin + p.split_cols);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds head `head`,
   // dims [16kk + 8kg, +8) for each 16-dim step kk.
@@ -409,10 +455,10 @@ void decode_kernel(DecodeParams p) {
       const int c = c0 + threadIdx.x;
       bool act = false;
       int code = 0;
-      if (c < seg1) {
-        const int r = p.indices[(int64_t)t * p.index_row_stride + c];
+      if (c < seg1 && tt.live(c)) {
+        const int r = tt.raw(c);
         if (r != -1) {
-          const bool swa = c < kSwaColumns;
+          const bool swa = c < tt.P;
           const int64_t rows = swa ? p.swa_rows : p.comp_rows;
           if (r >= 0 && (int64_t)r < rows) {
             act = true;
@@ -702,13 +748,13 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   // waiting for the table entries does not wait for Q.
   const int c_begin = s * p.split_cols;
   const int c_cap = min(p.K, c_begin + p.split_cols);
-  const int len_raw = p.topk_lens ? p.topk_lens[t] : p.K;
+  TokenTable tt = token_table(p, t);
+  const bool lens_ok = token_lengths(p, t, tt);
   int rv[CPT];
   auto load_idx = [&](int seg0, int seg_hi) {
     const int cb = seg0 + threadIdx.x * CPT;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k)
-      rv[k] = (cb + k < seg_hi) ? p.indices[(int64_t)t * p.index_row_stride + cb + k] : -1;
+    for (int k = 0; k < CPT; ++k) rv[k] = (cb + k < seg_hi) ? tt.raw(cb + k) : -1;
   };
   load_idx(c_begin, min(c_cap, c_begin + kSegHd));
   __builtin_amdgcn_sched_barrier(0);
@@ -729,10 +775,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 
   __builtin_amdgcn_sched_barrier(0);
-  if (p.validate && threadIdx.x == 0 && s == 0 && (len_raw < 0 || len_raw > p.K))
-    record_error(p.err, 2, t, -1);
-  const int len = min(max(len_raw, 0), p.K);
-  const int c_end = min(len, c_cap);
+  if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
+  const int c_end = min(tt.end(), c_cap);
 
   float m_run = -INFINITY;
   float l_run = 0.f;
@@ -876,8 +920,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     for (int k = 0; k < CPT; ++k) {
       const int c = cb + k;
       const int r = rv[k];
-      if (r != -1 && c < seg1) {
-        const int64_t rows = (c < kSwaColumns) ? p.swa_rows : p.comp_rows;
+      if (r != -1 && c < seg1 && tt.live(c)) {
+        const int64_t rows = (c < tt.P) ? p.swa_rows : p.comp_rows;
         if (r >= 0 && (int64_t)r < rows) actm |= 1u << k;
         else if (p.validate) record_error(p.err, 1, t, c);
       }
@@ -902,7 +946,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       if ((actm >> k) & 1u) {
-        last = (cb + k < kSwaColumns) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
+        last = (cb + k < tt.P) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
         slots[pos++] = last;
       }
     }

@@ -69,6 +69,17 @@ class DecodeArgs(ctypes.Structure):
     ]
 
 
+class Segments(ctypes.Structure):
+    """smla_segments: the two-segment form of the token tables."""
+    _fields_ = [
+        ("swa_indices", ctypes.c_void_p), ("swa_row_stride", ctypes.c_int64),
+        ("swa_topk_lens", ctypes.c_void_p),
+        ("extra_indices", ctypes.c_void_p), ("extra_row_stride", ctypes.c_int64),
+        ("extra_topk_lens", ctypes.c_void_p),
+        ("swa_width", ctypes.c_int32), ("extra_width", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -95,6 +106,10 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_decode.argtypes = [ctypes.POINTER(DecodeArgs),
                                       ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_decode.restype = ctypes.c_int
+    lib.sparse_mla_decode_segments.argtypes = [
+        ctypes.POINTER(DecodeArgs), ctypes.POINTER(Segments), ctypes.POINTER(Plan),
+        ctypes.c_void_p]
+    lib.sparse_mla_decode_segments.restype = ctypes.c_int
     lib.sparse_mla_gather_only.argtypes = [ctypes.POINTER(DecodeArgs),
                                            ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_gather_only.restype = ctypes.c_int
@@ -244,6 +259,66 @@ def decode(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
                      lse_scale=lse_scale, workspace=workspace, flags=flags)
     _check(load().sparse_mla_decode(ctypes.byref(args), ctypes.byref(plan),
                                     _stream(stream)), "sparse_mla_decode")
+    return plan
+
+
+def make_segments(swa_indices, extra_indices, swa_topk_lens=None,
+                  extra_topk_lens=None) -> Segments:
+    g = Segments()
+    g.swa_indices = _ptr(swa_indices)
+    g.swa_row_stride = 0 if swa_indices is None else int(swa_indices.stride(0))
+    g.swa_topk_lens = _ptr(swa_topk_lens)
+    g.extra_indices = _ptr(extra_indices)
+    g.extra_row_stride = 0 if extra_indices is None else int(extra_indices.stride(0))
+    g.extra_topk_lens = _ptr(extra_topk_lens)
+    g.swa_width = 0 if swa_indices is None else int(swa_indices.shape[1])
+    g.extra_width = 0 if extra_indices is None else int(extra_indices.shape[1])
+    return g
+
+
+def decode_segments(q, swa_pool, compressed_pool, swa_indices, extra_indices, out,
+                    *, swa_topk_lens=None, extra_topk_lens=None, out_lse=None,
+                    seq_lens=None, cum_seq_lens_q=None, sinks=None,
+                    bmm1_scale=1.0, bmm2_scale=1.0, lse_scale=1.0,
+                    workspace=None, plan: Optional[Plan] = None, flags=0,
+                    stream=None) -> Plan:
+    """sparse_mla_decode_segments: the two-segment form (an SWA table and an
+    extra compressed table, each with its own active length; either table
+    may be None).  Writes ``out`` (and ``out_lse``) in place and returns the
+    plan used, which is made for K = swa width + extra width."""
+    g = make_segments(swa_indices, extra_indices, swa_topk_lens, extra_topk_lens)
+    T, H = int(q.shape[0]), int(q.shape[1])
+    K = int(g.swa_width) + int(g.extra_width)
+    if plan is None:
+        plan = plan_splits(T, H, K, dtype_code(q), dtype_code(
+            swa_pool if swa_pool is not None else compressed_pool))
+    if workspace is None:
+        workspace = alloc_workspace(plan, T, H, flags, q.device)
+    a = DecodeArgs()
+    a.T, a.H, a.K = T, H, K
+    a.q_dtype = dtype_code(q)
+    a.q = _ptr(q)
+    a.swa_pool = _ptr(swa_pool)
+    a.swa_rows = 0 if swa_pool is None else int(swa_pool.shape[0])
+    a.compressed_pool = _ptr(compressed_pool)
+    a.compressed_rows = 0 if compressed_pool is None else int(compressed_pool.shape[0])
+    pool = swa_pool if swa_pool is not None else compressed_pool
+    a.kv_dtype = dtype_code(pool)
+    a.flags = flags
+    a.pool_row_stride = int(pool.stride(0))
+    a.seq_lens = _ptr(seq_lens)
+    a.cum_seq_lens_q = _ptr(cum_seq_lens_q)
+    a.num_requests = 0 if seq_lens is None else int(seq_lens.numel())
+    a.sinks = _ptr(sinks)
+    a.bmm1_scale, a.bmm2_scale, a.lse_scale = bmm1_scale, bmm2_scale, lse_scale
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * \
+        workspace.element_size()
+    _check(load().sparse_mla_decode_segments(ctypes.byref(a), ctypes.byref(g),
+                                             ctypes.byref(plan), _stream(stream)),
+           "sparse_mla_decode_segments")
     return plan
 
 

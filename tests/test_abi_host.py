@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {
         "sparse_mla_plan_splits", "sparse_mla_workspace_size",
         "sparse_mla_workspace_layout", "sparse_mla_decode",
-        "sparse_mla_gather_only",
+        "sparse_mla_gather_only", "sparse_mla_decode_segments",
         "sparse_mla_combine", "sparse_mla_get_device_error",
         "sparse_mla_status_string"}
     for n in names:
@@ -262,3 +262,91 @@ def test_gather_only_needs_no_outputs_and_checks_the_plan(so):
     p = plan(4, 128, 2048)
     p.K = 1024
     assert call_gather(so, a, p) == 6
+
+
+# ---------------------------------------------------------------------------
+# sparse_mla_decode_segments: the two-segment tables
+# ---------------------------------------------------------------------------
+
+def good_segments(K1=128, K2=1920):
+    g = L.Segments()
+    g.swa_indices = DUMMY if K1 else None
+    g.extra_indices = DUMMY + 4096 if K2 else None
+    g.swa_width, g.extra_width = K1, K2
+    return g
+
+
+def seg_args(T=4, K1=128, K2=1920):
+    a = good_args(T=T, K=K1 + K2)
+    a.indices = None
+    return a
+
+
+def call_seg(so, a, g, p=None):
+    if p is None:
+        p = plan(max(a.T, 1), a.H if a.H in (64, 128) else 128, max(a.K, 1))
+    return so.sparse_mla_decode_segments(ctypes.byref(a), ctypes.byref(g),
+                                         ctypes.byref(p), None)
+
+
+def bad_plan(a):
+    p = plan(max(a.T, 1), 128, max(a.K, 1))
+    p.K += 64      # rejected after every argument check
+    return p
+
+
+@pytest.mark.parametrize("K1,K2", [(128, 1920), (0, 300), (77, 0), (5, 61), (200, 5000)])
+def test_segments_pass_the_argument_checks(so, K1, K2):
+    a, g = seg_args(K1=K1, K2=K2), good_segments(K1, K2)
+    if K1 == 0:
+        a.swa_pool = None          # not needed without an SWA table
+    if K2 == 0:
+        a.compressed_pool = None   # nor the compressed pool without extras
+    assert call_seg(so, a, g, bad_plan(a)) == 6
+
+
+@pytest.mark.parametrize("change,code", [
+    ("null_seg", 1), ("widths", 1), ("neg_width", 1), ("indices_set", 1),
+    ("topk_set", 1), ("no_swa_table", 1), ("no_extra_table", 1),
+    ("no_swa_pool", 1), ("no_comp_pool", 1), ("swa_stride", 1),
+    ("extra_stride", 1), ("swa_misaligned", 5), ("extra_misaligned", 5),
+])
+def test_segments_rejects(so, change, code):
+    a, g = seg_args(), good_segments()
+    if change == "null_seg":
+        p = plan(4, 128, a.K)
+        assert so.sparse_mla_decode_segments(ctypes.byref(a), None, ctypes.byref(p),
+                                             None) == code
+        return
+    if change == "widths":
+        g.extra_width = 1900
+    elif change == "neg_width":
+        g.swa_width, g.extra_width = -1, 2049
+    elif change == "indices_set":
+        a.indices = DUMMY
+    elif change == "topk_set":
+        a.topk_lens = DUMMY
+    elif change == "no_swa_table":
+        g.swa_indices = None
+    elif change == "no_extra_table":
+        g.extra_indices = None
+    elif change == "no_swa_pool":
+        a.swa_pool = None
+    elif change == "no_comp_pool":
+        a.compressed_pool = None
+    elif change == "swa_stride":
+        g.swa_row_stride = 100
+    elif change == "extra_stride":
+        g.extra_row_stride = 1000
+    elif change == "swa_misaligned":
+        g.swa_indices = DUMMY + 2
+    elif change == "extra_misaligned":
+        g.extra_indices = DUMMY + 6
+    assert call_seg(so, a, g) == code
+
+
+def test_segments_zero_tokens_and_null_args(so):
+    g = good_segments()
+    assert so.sparse_mla_decode_segments(None, ctypes.byref(g), None, None) == 1
+    a = seg_args(T=0)
+    assert call_seg(so, a, g) == 0
