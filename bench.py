@@ -13,7 +13,9 @@ average launch duration, gathered bytes and FLOPs give the roofline numbers.
 
 Besides the headline numbers the line carries: the pure-gather rate on the
 same tables (sparse_mla_gather_only: compaction and row loads only, the
-attainable gather bandwidth), a cold-cache rate (a 1 GiB write between
+attainable gather bandwidth), the rate of the same call in the two-segment
+form (sparse_mla_decode_segments with a 128-column SWA table and a
+1920-column compressed table), a cold-cache rate (a 1 GiB write between
 launches evicts L2 and MALL), and with --sweep the per-T numbers for
 T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
 back-to-back launches.
@@ -225,6 +227,20 @@ def main():
         lib.gather_only(w.q, w.swa_pool, w.comp_pool, w.indices,
                         topk_lens=w.topk_lens, plan=plan, stream=stream)
     _, gper = time_launches(gather_step, max(args.steps // 2, 5), 3, stream)
+    # the same tables in the two-segment form (128-column SWA table with its
+    # length, 1920-column compressed table with its length)
+    swa_tab, extra_tab = w.indices[:, :128], w.indices[:, 128:]
+    swa_len = torch.clamp(w.topk_lens, max=128).int()
+    extra_len = torch.clamp(w.topk_lens - 128, min=0).int()
+
+    def seg_step():
+        lib.decode_segments(w.q, w.swa_pool, w.comp_pool, swa_tab, extra_tab, out,
+                            swa_topk_lens=swa_len, extra_topk_lens=extra_len,
+                            out_lse=lse, seq_lens=w.seq_lens, sinks=w.sinks,
+                            bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                            lse_scale=w.lse_scale, plan=plan, workspace=ws,
+                            stream=stream)
+    _, sper = time_launches(seg_step, max(args.steps // 2, 5), 3, stream)
     cold_ms = time_cold(step, 10, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -268,6 +284,7 @@ def main():
         "gather_only_GBps": round(gathered / (sum(gper) / len(gper) * 1e-3) / 1e9, 1),
         "decode_vs_gather_only": round((sum(gper) / len(gper)) / avg_launch_ms, 4),
         "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
+        "two_segment_GBps": round(gathered / (sum(sper) / len(sper) * 1e-3) / 1e9, 1),
         "plan": plan.as_dict(),
         "roofline": roofline,
     }
