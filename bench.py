@@ -240,7 +240,11 @@ def main():
                             bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
                             lse_scale=w.lse_scale, plan=plan, workspace=ws,
                             stream=stream)
-    _, sper = time_launches(seg_step, max(args.steps // 2, 5), 3, stream)
+    # alternate with the combined call so that both see the same clock
+    sper, cper = [], []
+    for _ in range(4):
+        sper += time_launches(seg_step, 8, 2, stream)[1]
+        cper += time_launches(step, 8, 2, stream)[1]
     cold_ms = time_cold(step, 10, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -285,6 +289,7 @@ def main():
         "decode_vs_gather_only": round((sum(gper) / len(gper)) / avg_launch_ms, 4),
         "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
         "two_segment_GBps": round(gathered / (sum(sper) / len(sper) * 1e-3) / 1e9, 1),
+        "two_segment_vs_combined": round((sum(cper) / len(cper)) / (sum(sper) / len(sper)), 4),
         "plan": plan.as_dict(),
         "roofline": roofline,
     }
