@@ -23,15 +23,17 @@ docstring says "parity unpinned".
 from .formats import bf16_bits_to_f64, e4m3fn_bits_to_f64, decode_bits, \
     round_to_bf16
 from .sparse_mla import (SWA_COLUMNS, active_slots, active_slots_segments,
-                         decode_token, sparse_mla_decode,
-                         sparse_mla_decode_segments, split_partials, combine,
-                         split_columns)
-from .brute import brute_force_decode, brute_force_decode_segments
+                         active_slots_paged, decode_token, sparse_mla_decode,
+                         sparse_mla_decode_segments, sparse_mla_decode_paged,
+                         split_partials, combine, split_columns)
+from .brute import (brute_force_decode, brute_force_decode_segments,
+                    brute_force_decode_paged)
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "decode_bits", "round_to_bf16",
-    "SWA_COLUMNS", "active_slots", "active_slots_segments", "decode_token",
-    "sparse_mla_decode", "sparse_mla_decode_segments", "split_partials",
+    "SWA_COLUMNS", "active_slots", "active_slots_segments",
+    "active_slots_paged", "decode_token", "sparse_mla_decode",
+    "sparse_mla_decode_segments", "sparse_mla_decode_paged", "split_partials",
     "combine", "split_columns", "brute_force_decode",
-    "brute_force_decode_segments",
+    "brute_force_decode_segments", "brute_force_decode_paged",
 ]

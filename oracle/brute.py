@@ -58,6 +58,43 @@ def _segments_multiset(swa_indices, swa_lens, extra_indices, extra_lens, t):
     return mult
 
 
+def _paged_multiset(swa_indices, swa_lens, block_tables, page_size, total_lens, t):
+    """Multiset of (pool, row) of token t in the page-table form: its
+    visible window rows, then compressed rows numbered page by page."""
+    mult = Counter()
+    k1 = 0 if swa_indices is None else swa_indices.shape[1]
+    w = k1 if swa_lens is None else max(0, min(int(swa_lens[t]), k1))
+    for c in range(w):
+        r = int(swa_indices[t][c])
+        if r != -1:
+            mult[(0, r)] += 1
+    if block_tables is None:
+        return mult
+    pages = [int(x) for x in block_tables[t]]
+    cap = len(pages) * page_size
+    n = cap if total_lens is None else max(0, min(int(total_lens[t]) - w, cap))
+    done = 0
+    for pg in pages:
+        for off in range(page_size):
+            if done == n:
+                return mult
+            mult[(1, pg * page_size + off)] += 1
+            done += 1
+    return mult
+
+
+def brute_force_decode_paged(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                             swa_indices, block_tables, page_size, swa_lens,
+                             total_lens, sinks, bmm1_scale, bmm2_scale,
+                             lse_scale, dps: int = 50):
+    """The page-table form by the same multiset evaluation.  Returns
+    (out, lse)."""
+    return _brute(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
+                  lambda t: _paged_multiset(swa_indices, swa_lens, block_tables,
+                                            page_size, total_lens, t),
+                  sinks, bmm1_scale, bmm2_scale, lse_scale, dps)
+
+
 def brute_force_decode(q_bits, q_dtype, swa_bits, comp_bits, kv_dtype,
                        indices, topk_lens, sinks, bmm1_scale, bmm2_scale,
                        lse_scale, dps: int = 50):

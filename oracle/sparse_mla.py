@@ -43,8 +43,13 @@ Two-segment form (``sparse_mla_decode_segments``): the same definition
 with A_t = the active slots of an SWA table (length swa_topk_lens[t]) and of
 an extra compressed table (length extra_topk_lens[t]) together.
 
+Page-table form (``sparse_mla_decode_paged``): the window entries of an SWA
+row plus the canonical page expansion of a block-table row of the
+compressed pool.
+
 Parity status: pinned (tests/test_oracle_pins.py, and for the two-segment
-form tests/test_oracle_segments.py) by an independent
+and page-table forms tests/test_oracle_segments.py and
+tests/test_oracle_paged.py) by an independent
 multiset brute force in arbitrary precision, closed forms, invariants and
 torch's float64 scaled_dot_product_attention, except that "out_lse includes
 the sink" is a reading the pages do not settle (parity unpinned for that
@@ -109,6 +114,39 @@ def active_slots_segments(swa_row, swa_len: Optional[int], extra_row,
         r = int(extra_row[j])
         if r != -1:
             out.append((K1 + j, 1, r))
+    return out
+
+
+def active_slots_paged(swa_row, swa_len: Optional[int], block_row,
+                       page_size: int, total_len: Optional[int]):
+    """Active slots of one token in the page-table form, as (column, pool,
+    row): FlashInfer ``trtllm_batch_decode_sparse_mla_dsv4`` (introduction,
+    the HCA paragraph: the SWA stream takes physical token rows, the
+    compressed stream physical page IDs; parameters ``hca_swa_indices``,
+    ``swa_topk_lens``, ``hca_compressed_block_tables``, ``sparse_topk_lens``
+    and, under ``hca_sparse_indices_format``, the canonical expansion
+    page_id * page_size + page_offset).  Reading: the first ``swa_len``
+    entries of the SWA row are the visible window (None = all); the token's
+    compressed slots are the canonical expansion of its block-table row, in
+    order, and the first ``total_len - swa_len`` of them are visible
+    (``sparse_topk_lens`` counts window plus compressed slots; None = every
+    slot of the table).  A -1 SWA entry masks its slot.  Compressed slot j
+    has column K1 + j (K1 = the SWA row's width)."""
+    K1 = 0 if swa_row is None else int(np.asarray(swa_row).shape[0])
+    P = 0 if block_row is None else int(np.asarray(block_row).shape[0])
+    K2 = P * int(page_size)
+    n1 = K1 if swa_len is None else int(swa_len)
+    n1 = max(0, min(n1, K1))
+    tot = K1 + K2 if total_len is None else int(total_len)
+    n2 = max(0, min(tot - n1, K2))
+    out = []
+    for c in range(n1):
+        r = int(swa_row[c])
+        if r != -1:
+            out.append((c, 0, r))
+    for j in range(n2):
+        page = int(block_row[j // page_size])
+        out.append((K1 + j, 1, page * int(page_size) + j % int(page_size)))
     return out
 
 
@@ -205,6 +243,40 @@ def sparse_mla_decode_segments(q_bits, q_dtype: str, swa_bits, comp_bits,
             None if swa_topk_lens is None else int(swa_topk_lens[t]),
             None if extra_indices is None else np.asarray(extra_indices[t]),
             None if extra_topk_lens is None else int(extra_topk_lens[t]))
+        rows = gather_rows(slots, swa_bits, comp_bits, kv_dtype)
+        q_t = decode_bits(q_bits[t], q_dtype)
+        o, l, lns = decode_token(q_t, rows, sk, b1, b2, g)
+        outs.append(o)
+        lses.append(l)
+        lses_ns.append(lns)
+        nact.append(len(slots))
+    return {"out": np.stack(outs), "lse": np.stack(lses),
+            "lse_nosink": np.stack(lses_ns), "n_active": np.array(nact)}
+
+
+def sparse_mla_decode_paged(q_bits, q_dtype: str, swa_bits, comp_bits,
+                            kv_dtype: str, swa_indices, block_tables,
+                            page_size: int, swa_topk_lens=None, topk_lens=None,
+                            sinks=None, bmm1_scale: float = 1.0,
+                            bmm2_scale: float = 1.0, lse_scale: float = 1.0,
+                            tokens: Optional[Sequence[int]] = None):
+    """The page-table form (see ``active_slots_paged``): swa_indices [T,K1]
+    with swa_topk_lens [T] (visible window), block_tables [T,max_pages] of
+    compressed-pool page IDs with ``page_size`` rows per page, and
+    topk_lens [T] = visible window + compressed slots.  Everything after the
+    selection is ``decode_token``.  Returns the same dict as
+    ``sparse_mla_decode``."""
+    T = q_bits.shape[0]
+    tokens = range(T) if tokens is None else list(tokens)
+    b1, b2, g = _fp32(bmm1_scale), _fp32(bmm2_scale), _fp32(lse_scale)
+    sk = None if sinks is None else np.asarray(sinks, np.float32).astype(np.float64)
+    outs, lses, lses_ns, nact = [], [], [], []
+    for t in tokens:
+        slots = active_slots_paged(
+            None if swa_indices is None else np.asarray(swa_indices[t]),
+            None if swa_topk_lens is None else int(swa_topk_lens[t]),
+            None if block_tables is None else np.asarray(block_tables[t]),
+            page_size, None if topk_lens is None else int(topk_lens[t]))
         rows = gather_rows(slots, swa_bits, comp_bits, kv_dtype)
         q_t = decode_bits(q_bits[t], q_dtype)
         o, l, lns = decode_token(q_t, rows, sk, b1, b2, g)
