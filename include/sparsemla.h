@@ -223,6 +223,51 @@ int sparse_mla_decode_segments(const smla_decode_args* args,
                                const smla_segments* seg, const smla_plan* plan,
                                smla_stream_t stream);
 
+/* The page-table form (FlashInfer "trtllm_batch_decode_sparse_mla_dsv4",
+ * introduction (HCA paragraph: the SWA stream takes physical token rows,
+ * the compressed stream physical page IDs) and parameters
+ * "hca_swa_indices", "swa_topk_lens", "hca_compressed_block_tables",
+ * "sparse_topk_lens", "hca_seq_lens" and "hca_sparse_indices_format" (the
+ * canonical expansion page_id * page_size + page_offset)): token t attends
+ * to the first swa_topk_lens[t] rows of its window row and to the first
+ * args->topk_lens[t] - swa_topk_lens[t] slots of the page expansion of its
+ * block-table row, compressed slot j being row
+ * block_tables[t][j / page_size] * page_size + j % page_size of
+ * compressed_pool.  A -1 window entry masks its slot; a page whose rows
+ * fall outside the pool is skipped (reported in validate mode).  Device
+ * pointers; the caller owns them. */
+typedef struct smla_paged {
+  const int32_t* swa_indices;     /* [T, swa_row_stride] window rows of swa_pool
+                                     (NULL iff swa_width == 0) */
+  int64_t swa_row_stride;         /* elements; 0 means swa_width */
+  const int32_t* swa_topk_lens;   /* [T] visible window rows in [0, swa_width], or
+                                     NULL = swa_width */
+  const int32_t* block_tables;    /* [T, block_table_stride] page IDs of
+                                     compressed_pool (NULL iff max_pages == 0) */
+  int64_t block_table_stride;     /* elements; 0 means max_pages */
+  const int32_t* hca_seq_lens;    /* [num_requests] or NULL; accepted, unused by the
+                                     math (a scheduling hint on the pages) */
+  int32_t swa_width;              /* >= 0 (128 on the pages) */
+  int32_t max_pages;              /* >= 0 */
+  int32_t page_size;              /* rows per compressed page, >= 1 */
+  int32_t reserved;
+} smla_paged;
+
+/* sparse_mla_decode with the page-table form.  args->K must be
+ * swa_width + max_pages * page_size (window columns first, then compressed
+ * slots: the row the split plan cuts and validation errors report);
+ * args->indices must be NULL; args->topk_lens is the visible window +
+ * compressed slot count (NULL = every slot; a count below the window or
+ * beyond the table is clamped and, in validate mode, reported as
+ * SMLA_DEVERR_TOPK_LEN, as is a window length outside [0, swa_width]).
+ * Everything else as sparse_mla_decode.  Returns SMLA_ERR_INVALID_ARG for a
+ * NULL pg, a bad width, page count or page size, a K that does not match,
+ * a missing table or pool for a non-zero width, a row stride below its
+ * width, or a non-NULL args->indices.  Asynchronous, no allocation, graph
+ * capturable. */
+int sparse_mla_decode_paged(const smla_decode_args* args, const smla_paged* pg,
+                            const smla_plan* plan, smla_stream_t stream);
+
 /* Measurement aid (not part of the method): run only the table compaction
  * and the row gather of sparse_mla_decode on the same arguments and plan,
  * with no arithmetic and no output, to give the attainable gathered-row

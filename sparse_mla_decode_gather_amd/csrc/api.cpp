@@ -166,10 +166,12 @@ namespace {
 // Argument checks shared by sparse_mla_decode and sparse_mla_gather_only,
 // and the kernel parameters they resolve to.  *plan is replaced by
 // *local when the caller passed none.  Returns SMLA_OK or a status.
-// seg == NULL: the combined table (args->indices, args->topk_lens); else the
-// two-segment form, where args->indices and args->topk_lens must be NULL.
+// seg == pg == NULL: the combined table (args->indices, args->topk_lens);
+// seg: the two-segment form; pg: the page-table form.  In both of the
+// latter args->indices must be NULL; args->topk_lens must be NULL for seg
+// and is the window + compressed slot count for pg.
 int prepare_call(const smla_decode_args* a, const smla_segments* seg,
-                 const smla_plan*& plan, smla_plan* local,
+                 const smla_paged* pg, const smla_plan*& plan, smla_plan* local,
                  bool with_outputs, smla::DecodeParams* p, Layout* L) {
   if (!a) return SMLA_ERR_INVALID_ARG;
   if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
@@ -179,7 +181,22 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   int k1, k2;
   const int32_t *t1, *t2;
   int64_t s1, s2;
-  if (seg) {
+  int64_t t2_width;   // elements of a row of the second table that are read
+  if (pg) {
+    if (pg->swa_width < 0 || pg->max_pages < 0 || pg->page_size < 1)
+      return SMLA_ERR_INVALID_ARG;
+    const int64_t slots = (int64_t)pg->max_pages * pg->page_size;
+    if (slots > INT_MAX / 2 || (int64_t)pg->swa_width + slots != a->K)
+      return SMLA_ERR_INVALID_ARG;
+    if (a->indices) return SMLA_ERR_INVALID_ARG;
+    k1 = pg->swa_width;
+    k2 = (int)slots;
+    t1 = pg->swa_indices;
+    t2 = pg->block_tables;
+    s1 = pg->swa_row_stride == 0 ? k1 : pg->swa_row_stride;
+    s2 = pg->block_table_stride == 0 ? pg->max_pages : pg->block_table_stride;
+    t2_width = pg->max_pages;
+  } else if (seg) {
     if (seg->swa_width < 0 || seg->extra_width < 0 ||
         (int64_t)seg->swa_width + seg->extra_width != a->K)
       return SMLA_ERR_INVALID_ARG;
@@ -190,6 +207,7 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
     t2 = seg->extra_indices;
     s1 = seg->swa_row_stride == 0 ? k1 : seg->swa_row_stride;
     s2 = seg->extra_row_stride == 0 ? k2 : seg->extra_row_stride;
+    t2_width = k2;
   } else {
     k1 = std::min(a->K, smla::kSwaColumns);
     k2 = a->K - k1;
@@ -198,11 +216,12 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
     if (s1 < a->K) return SMLA_ERR_INVALID_ARG;
     t2 = a->indices ? a->indices + k1 : nullptr;
     s2 = s1;
+    t2_width = k2;
   }
   if (a->T == 0) return SMLA_OK;
   if (!a->q || (with_outputs && !a->out)) return SMLA_ERR_INVALID_ARG;
   if (k1 > 0 && (!t1 || !a->swa_pool || s1 < k1)) return SMLA_ERR_INVALID_ARG;
-  if (k2 > 0 && (!t2 || !a->compressed_pool || s2 < k2)) return SMLA_ERR_INVALID_ARG;
+  if (k2 > 0 && (!t2 || !a->compressed_pool || s2 < t2_width)) return SMLA_ERR_INVALID_ARG;
   if (a->swa_rows < 0 || a->compressed_rows < 0) return SMLA_ERR_INVALID_ARG;
   if ((int64_t)a->T * a->H > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
   const int64_t row_stride = a->pool_row_stride == 0 ? smla::kHeadDim : a->pool_row_stride;
@@ -247,11 +266,12 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   p->index_row_stride = k1 > 0 ? s1 : s2;
   p->indices2 = k2 > 0 ? t2 : t1;
   p->index_row_stride2 = k2 > 0 ? s2 : s1;
-  p->swa_cols = seg ? k1 : smla::kSwaColumns;
+  p->swa_cols = (seg || pg) ? k1 : smla::kSwaColumns;
   p->K2 = k2;
-  p->segmented = seg ? 1 : 0;
-  p->topk_lens = seg ? seg->swa_topk_lens : a->topk_lens;
-  p->lens2 = seg ? seg->extra_topk_lens : nullptr;
+  p->segmented = pg ? 2 : seg ? 1 : 0;
+  p->page_size = pg ? pg->page_size : 0;
+  p->topk_lens = pg ? pg->swa_topk_lens : seg ? seg->swa_topk_lens : a->topk_lens;
+  p->lens2 = pg ? a->topk_lens : seg ? seg->extra_topk_lens : nullptr;
   p->sinks = a->sinks;
   p->scale_log2 = (float)((double)a->bmm1_scale * 1.4426950408889634);
   p->bmm2 = a->bmm2_scale;
@@ -306,7 +326,18 @@ int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
   smla_plan local;
   smla::DecodeParams p;
   Layout L;
-  const int st = prepare_call(a, nullptr, plan, &local, true, &p, &L);
+  const int st = prepare_call(a, nullptr, nullptr, plan, &local, true, &p, &L);
+  if (st != SMLA_OK || a->T == 0) return st;
+  return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
+}
+
+int sparse_mla_decode_paged(const smla_decode_args* a, const smla_paged* pg,
+                            const smla_plan* plan, smla_stream_t stream_handle) {
+  if (!pg) return SMLA_ERR_INVALID_ARG;
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  const int st = prepare_call(a, nullptr, pg, plan, &local, true, &p, &L);
   if (st != SMLA_OK || a->T == 0) return st;
   return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
 }
@@ -317,7 +348,7 @@ int sparse_mla_decode_segments(const smla_decode_args* a, const smla_segments* s
   smla_plan local;
   smla::DecodeParams p;
   Layout L;
-  const int st = prepare_call(a, seg, plan, &local, true, &p, &L);
+  const int st = prepare_call(a, seg, nullptr, plan, &local, true, &p, &L);
   if (st != SMLA_OK || a->T == 0) return st;
   return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
 }
@@ -327,7 +358,7 @@ int sparse_mla_gather_only(const smla_decode_args* a, const smla_plan* plan,
   smla_plan local;
   smla::DecodeParams p;
   Layout L;
-  const int st = prepare_call(a, nullptr, plan, &local, false, &p, &L);
+  const int st = prepare_call(a, nullptr, nullptr, plan, &local, false, &p, &L);
   if (st != SMLA_OK || a->T == 0) return st;
   if (a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (a->q_dtype != SMLA_DTYPE_BF16 || a->kv_dtype != SMLA_DTYPE_BF16)

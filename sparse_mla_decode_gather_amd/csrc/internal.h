@@ -37,16 +37,18 @@ struct DecodeParams {
   int32_t validate;
   // The token's columns [0, K) split in two tables: columns < swa_cols read
   // `indices` (SWA pool), the others read `indices2` at column - swa_cols
-  // (compressed pool).  Combined form: indices2 = indices + 128 and
-  // topk_lens counts both; two-segment form (segmented = 1): topk_lens
-  // counts the first table's active columns and lens2 the second's.
+  // (compressed pool).  segmented = 0, combined form: indices2 = indices +
+  // 128 and topk_lens counts both.  1, two segments: topk_lens counts the
+  // first table's active columns and lens2 the second's.  2, page table:
+  // indices2 holds compressed-pool page IDs of page_size rows, topk_lens
+  // counts the visible window and lens2 window + compressed slots.
   const int32_t* indices2;
   int64_t index_row_stride2;
-  const int32_t* lens2;          // [T] or null (= K2)
+  const int32_t* lens2;          // [T] or null
   int32_t swa_cols;
-  int32_t K2;                    // width of the second table
+  int32_t K2;                    // columns of the second table (slots when paged)
   int32_t segmented;
-  int32_t pad_;
+  int32_t page_size;             // > 0 only when segmented == 2
 };
 
 struct CombineParams {

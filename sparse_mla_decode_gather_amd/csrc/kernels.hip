@@ -210,14 +210,25 @@ __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
 // 128 SWA columns, one length counting both) and the two-segment form (same
 // page, "swa_topk_lens"/"extra_sparse_indices"/"extra_sparse_topk_lens";
 // the Cake page's "extra_indices"/"extra_topk_length": one length per
-// table) differ only in where the tables and lengths come from.
+// table) differ only in where the tables and lengths come from.  In the
+// page-table form (same page, HCA paragraph, "hca_compressed_block_tables")
+// the second table holds page IDs and compressed slot j is row
+// page[j / ps] * ps + j % ps.
 struct TokenTable {
   const int32_t* row1;
   const int32_t* row2;
   int P;        // columns of the first table
+  int ps;       // rows per page when the second table holds page IDs, else 0
   int L1, L2;   // active columns of each table
-  // the stored entry of column c (whether or not the column is active)
-  __device__ __forceinline__ int raw(int c) const { return c < P ? row1[c] : row2[c - P]; }
+  // the stored entry of column c (whether or not the column is active); a
+  // page-table row that does not fit an int comes back as -2 (invalid)
+  __device__ __forceinline__ int raw(int c) const {
+    if (c < P) return row1[c];
+    const int j = c - P;
+    if (ps == 0) return row2[j];
+    const int64_t r = (int64_t)row2[j / ps] * ps + j % ps;
+    return (r >= 0 && r <= 0x7FFFFFFF) ? (int)r : -2;
+  }
   // column c is below its table's length
   __device__ __forceinline__ bool live(int c) const { return c < P ? c < L1 : c - P < L2; }
   // one past the last column that can be active
@@ -229,6 +240,7 @@ __device__ __forceinline__ TokenTable token_table(const DecodeParams& p, int t) 
   tt.P = p.swa_cols;
   tt.row1 = p.indices + (int64_t)t * p.index_row_stride;
   tt.row2 = p.indices2 + (int64_t)t * p.index_row_stride2;
+  tt.ps = p.segmented == 2 ? p.page_size : 0;
   tt.L1 = tt.L2 = 0;
   return tt;
 }
@@ -236,6 +248,15 @@ __device__ __forceinline__ TokenTable token_table(const DecodeParams& p, int t) 
 // Reads the token's length(s) into tt (clamped to the tables) and reports
 // whether they were in range.
 __device__ __forceinline__ bool token_lengths(const DecodeParams& p, int t, TokenTable& tt) {
+  if (p.segmented == 2) {
+    // visible window, then window + compressed slots
+    const int a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
+    const int tot = p.lens2 ? p.lens2[t] : p.swa_cols + p.K2;
+    tt.L1 = min(max(a, 0), p.swa_cols);
+    const int n = tot - tt.L1;
+    tt.L2 = min(max(n, 0), p.K2);
+    return a >= 0 && a <= p.swa_cols && n >= 0 && n <= p.K2;
+  }
   if (p.segmented) {
     const int a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
     const int b = p.lens2 ? p.lens2[t] : p.K2;

@@ -80,6 +80,18 @@ class Segments(ctypes.Structure):
     ]
 
 
+class Paged(ctypes.Structure):
+    """smla_paged: window rows plus a compressed-pool page table."""
+    _fields_ = [
+        ("swa_indices", ctypes.c_void_p), ("swa_row_stride", ctypes.c_int64),
+        ("swa_topk_lens", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
+        ("hca_seq_lens", ctypes.c_void_p),
+        ("swa_width", ctypes.c_int32), ("max_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 
@@ -110,6 +122,10 @@ def load() -> ctypes.CDLL:
         ctypes.POINTER(DecodeArgs), ctypes.POINTER(Segments), ctypes.POINTER(Plan),
         ctypes.c_void_p]
     lib.sparse_mla_decode_segments.restype = ctypes.c_int
+    lib.sparse_mla_decode_paged.argtypes = [
+        ctypes.POINTER(DecodeArgs), ctypes.POINTER(Paged), ctypes.POINTER(Plan),
+        ctypes.c_void_p]
+    lib.sparse_mla_decode_paged.restype = ctypes.c_int
     lib.sparse_mla_gather_only.argtypes = [ctypes.POINTER(DecodeArgs),
                                            ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_gather_only.restype = ctypes.c_int
@@ -276,6 +292,72 @@ def make_segments(swa_indices, extra_indices, swa_topk_lens=None,
     return g
 
 
+def _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, topk_lens,
+                        seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
+                        lse_scale, workspace, flags) -> DecodeArgs:
+    a = DecodeArgs()
+    a.T, a.H, a.K = int(q.shape[0]), int(q.shape[1]), K
+    a.q_dtype = dtype_code(q)
+    a.q = _ptr(q)
+    a.swa_pool = _ptr(swa_pool)
+    a.swa_rows = 0 if swa_pool is None else int(swa_pool.shape[0])
+    a.compressed_pool = _ptr(compressed_pool)
+    a.compressed_rows = 0 if compressed_pool is None else int(compressed_pool.shape[0])
+    pool = swa_pool if swa_pool is not None else compressed_pool
+    a.kv_dtype = dtype_code(pool)
+    a.flags = flags
+    a.pool_row_stride = int(pool.stride(0))
+    a.topk_lens = _ptr(topk_lens)
+    a.seq_lens = _ptr(seq_lens)
+    a.cum_seq_lens_q = _ptr(cum_seq_lens_q)
+    a.num_requests = 0 if seq_lens is None else int(seq_lens.numel())
+    a.sinks = _ptr(sinks)
+    a.bmm1_scale, a.bmm2_scale, a.lse_scale = bmm1_scale, bmm2_scale, lse_scale
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = 0 if workspace is None else workspace.numel() * \
+        workspace.element_size()
+    return a
+
+
+def decode_paged(q, swa_pool, compressed_pool, swa_indices, block_tables,
+                 page_size: int, out, *, swa_topk_lens=None, topk_lens=None,
+                 hca_seq_lens=None, out_lse=None, seq_lens=None,
+                 cum_seq_lens_q=None, sinks=None, bmm1_scale=1.0, bmm2_scale=1.0,
+                 lse_scale=1.0, workspace=None, plan: Optional[Plan] = None,
+                 flags=0, stream=None) -> Plan:
+    """sparse_mla_decode_paged: window rows (``swa_indices``, visible
+    ``swa_topk_lens``) plus the page expansion of ``block_tables`` (page IDs
+    of ``page_size`` compressed rows); ``topk_lens`` counts window +
+    compressed slots.  Writes ``out`` (and ``out_lse``) in place and returns
+    the plan used, made for K = window width + pages * page_size."""
+    g = Paged()
+    g.swa_indices = _ptr(swa_indices)
+    g.swa_row_stride = 0 if swa_indices is None else int(swa_indices.stride(0))
+    g.swa_topk_lens = _ptr(swa_topk_lens)
+    g.block_tables = _ptr(block_tables)
+    g.block_table_stride = 0 if block_tables is None else int(block_tables.stride(0))
+    g.hca_seq_lens = _ptr(hca_seq_lens)
+    g.swa_width = 0 if swa_indices is None else int(swa_indices.shape[1])
+    g.max_pages = 0 if block_tables is None else int(block_tables.shape[1])
+    g.page_size = int(page_size)
+    T, H = int(q.shape[0]), int(q.shape[1])
+    K = int(g.swa_width) + int(g.max_pages) * int(page_size)
+    if plan is None:
+        plan = plan_splits(T, H, K, dtype_code(q), dtype_code(
+            swa_pool if swa_pool is not None else compressed_pool))
+    if workspace is None:
+        workspace = alloc_workspace(plan, T, H, flags, q.device)
+    a = _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, topk_lens,
+                            seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
+                            lse_scale, workspace, flags)
+    _check(load().sparse_mla_decode_paged(ctypes.byref(a), ctypes.byref(g),
+                                          ctypes.byref(plan), _stream(stream)),
+           "sparse_mla_decode_paged")
+    return plan
+
+
 def decode_segments(q, swa_pool, compressed_pool, swa_indices, extra_indices, out,
                     *, swa_topk_lens=None, extra_topk_lens=None, out_lse=None,
                     seq_lens=None, cum_seq_lens_q=None, sinks=None,
@@ -294,28 +376,9 @@ def decode_segments(q, swa_pool, compressed_pool, swa_indices, extra_indices, ou
             swa_pool if swa_pool is not None else compressed_pool))
     if workspace is None:
         workspace = alloc_workspace(plan, T, H, flags, q.device)
-    a = DecodeArgs()
-    a.T, a.H, a.K = T, H, K
-    a.q_dtype = dtype_code(q)
-    a.q = _ptr(q)
-    a.swa_pool = _ptr(swa_pool)
-    a.swa_rows = 0 if swa_pool is None else int(swa_pool.shape[0])
-    a.compressed_pool = _ptr(compressed_pool)
-    a.compressed_rows = 0 if compressed_pool is None else int(compressed_pool.shape[0])
-    pool = swa_pool if swa_pool is not None else compressed_pool
-    a.kv_dtype = dtype_code(pool)
-    a.flags = flags
-    a.pool_row_stride = int(pool.stride(0))
-    a.seq_lens = _ptr(seq_lens)
-    a.cum_seq_lens_q = _ptr(cum_seq_lens_q)
-    a.num_requests = 0 if seq_lens is None else int(seq_lens.numel())
-    a.sinks = _ptr(sinks)
-    a.bmm1_scale, a.bmm2_scale, a.lse_scale = bmm1_scale, bmm2_scale, lse_scale
-    a.out = _ptr(out)
-    a.out_lse = _ptr(out_lse)
-    a.workspace = _ptr(workspace)
-    a.workspace_bytes = 0 if workspace is None else workspace.numel() * \
-        workspace.element_size()
+    a = _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, None,
+                            seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
+                            lse_scale, workspace, flags)
     _check(load().sparse_mla_decode_segments(ctypes.byref(a), ctypes.byref(g),
                                              ctypes.byref(plan), _stream(stream)),
            "sparse_mla_decode_segments")

@@ -31,6 +31,7 @@ def test_every_declared_symbol_is_exported(so):
         "sparse_mla_plan_splits", "sparse_mla_workspace_size",
         "sparse_mla_workspace_layout", "sparse_mla_decode",
         "sparse_mla_gather_only", "sparse_mla_decode_segments",
+        "sparse_mla_decode_paged",
         "sparse_mla_combine", "sparse_mla_get_device_error",
         "sparse_mla_status_string"}
     for n in names:
@@ -350,3 +351,78 @@ def test_segments_zero_tokens_and_null_args(so):
     assert so.sparse_mla_decode_segments(None, ctypes.byref(g), None, None) == 1
     a = seg_args(T=0)
     assert call_seg(so, a, g) == 0
+
+
+# ---------------------------------------------------------------------------
+# sparse_mla_decode_paged: window rows + compressed page table
+# ---------------------------------------------------------------------------
+
+def good_paged(K1=128, pages=30, ps=64):
+    g = L.Paged()
+    g.swa_indices = DUMMY if K1 else None
+    g.block_tables = DUMMY + 8192 if pages else None
+    g.swa_width, g.max_pages, g.page_size = K1, pages, ps
+    return g
+
+
+def paged_args(T=4, K1=128, pages=30, ps=64):
+    a = good_args(T=T, K=K1 + pages * ps)
+    a.indices = None
+    return a
+
+
+def call_paged(so, a, g, p=None):
+    if p is None:
+        p = plan(max(a.T, 1), a.H if a.H in (64, 128) else 128, max(a.K, 1))
+    return so.sparse_mla_decode_paged(ctypes.byref(a), ctypes.byref(g), ctypes.byref(p), None)
+
+
+@pytest.mark.parametrize("K1,pages,ps", [(128, 30, 64), (0, 5, 64), (128, 0, 64), (7, 3, 1),
+                                         (100, 9, 37)])
+def test_paged_pass_the_argument_checks(so, K1, pages, ps):
+    a, g = paged_args(K1=K1, pages=pages, ps=ps), good_paged(K1, pages, ps)
+    if K1 == 0:
+        a.swa_pool = None
+    if pages == 0:
+        a.compressed_pool = None
+    a.topk_lens = DUMMY            # the window + compressed count is allowed here
+    assert call_paged(so, a, g, bad_plan(a)) == 6
+
+
+@pytest.mark.parametrize("change,code", [
+    ("null", 1), ("K", 1), ("page_size", 1), ("neg_pages", 1), ("neg_width", 1),
+    ("indices_set", 1), ("no_swa_table", 1), ("no_block_table", 1), ("no_comp_pool", 1),
+    ("swa_stride", 1), ("block_stride", 1), ("huge", 1), ("block_misaligned", 5),
+])
+def test_paged_rejects(so, change, code):
+    a, g = paged_args(), good_paged()
+    if change == "null":
+        p = plan(4, 128, a.K)
+        assert so.sparse_mla_decode_paged(ctypes.byref(a), None, ctypes.byref(p), None) == code
+        return
+    if change == "K":
+        a.K += 1
+    elif change == "page_size":
+        g.page_size = 0
+    elif change == "neg_pages":
+        g.max_pages = -1
+    elif change == "neg_width":
+        g.swa_width = -3
+    elif change == "indices_set":
+        a.indices = DUMMY
+    elif change == "no_swa_table":
+        g.swa_indices = None
+    elif change == "no_block_table":
+        g.block_tables = None
+    elif change == "no_comp_pool":
+        a.compressed_pool = None
+    elif change == "swa_stride":
+        g.swa_row_stride = 127
+    elif change == "block_stride":
+        g.block_table_stride = 29
+    elif change == "huge":
+        g.max_pages, g.page_size = 1 << 20, 1 << 12
+        a.K = 128
+    elif change == "block_misaligned":
+        g.block_tables = DUMMY + 2
+    assert call_paged(so, a, g) == code
