@@ -15,7 +15,10 @@ Besides the headline numbers the line carries: the pure-gather rate on the
 same tables (sparse_mla_gather_only: compaction and row loads only, the
 attainable gather bandwidth), the rate of the same call in the two-segment
 form (sparse_mla_decode_segments with a 128-column SWA table and a
-1920-column compressed table), a cold-cache rate (a 1 GiB write between
+1920-column compressed table), the rate of the page-table form
+(sparse_mla_decode_paged: the same 128 window rows plus 30 random pages of
+64 consecutive compressed rows per token; same gathered bytes, page-local
+rows), a cold-cache rate (a 1 GiB write between
 launches evicts L2 and MALL), and with --sweep the per-T numbers for
 T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
 back-to-back launches.
@@ -245,6 +248,27 @@ def main():
     for _ in range(4):
         sper += time_launches(seg_step, 8, 2, stream)[1]
         cper += time_launches(step, 8, 2, stream)[1]
+    # page-table form at the same size: the 128 window rows plus 30 pages of
+    # 64 consecutive compressed rows per token (page IDs drawn without
+    # repeats from the token's own 512-page compressed region)
+    ps, npg = 64, (w.K - 128) // 64
+    region = w.comp_pool.shape[0] // T // ps
+    gen = torch.Generator().manual_seed(77)
+    bt = torch.stack([torch.randperm(region, generator=gen)[:npg] + t * region
+                      for t in range(T)]).int().cuda()
+    tot = torch.full((T,), w.K, dtype=torch.int32, device="cuda")
+
+    def paged_step():
+        lib.decode_paged(w.q, w.swa_pool, w.comp_pool, swa_tab, bt, ps, out,
+                         swa_topk_lens=swa_len, topk_lens=tot, out_lse=lse,
+                         seq_lens=w.seq_lens, sinks=w.sinks,
+                         bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                         lse_scale=w.lse_scale, plan=plan, workspace=ws,
+                         stream=stream)
+    pper, cper2 = [], []
+    for _ in range(4):
+        pper += time_launches(paged_step, 8, 2, stream)[1]
+        cper2 += time_launches(step, 8, 2, stream)[1]
     cold_ms = time_cold(step, 10, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -290,6 +314,8 @@ def main():
         "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
         "two_segment_GBps": round(gathered / (sum(sper) / len(sper) * 1e-3) / 1e9, 1),
         "two_segment_vs_combined": round((sum(cper) / len(cper)) / (sum(sper) / len(sper)), 4),
+        "paged_GBps": round(gathered / (sum(pper) / len(pper) * 1e-3) / 1e9, 1),
+        "paged_vs_combined": round((sum(cper2) / len(cper2)) / (sum(pper) / len(pper)), 4),
         "plan": plan.as_dict(),
         "roofline": roofline,
     }
