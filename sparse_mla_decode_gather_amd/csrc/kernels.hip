@@ -214,7 +214,15 @@ __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
 // page-table form (same page, HCA paragraph, "hca_compressed_block_tables")
 // the second table holds page IDs and compressed slot j is row
 // page[j / ps] * ps + j % ps.
+//
+// GEN = false is the combined form only (one row, 128 SWA columns, one
+// length), compiled to a plain indexed load: the general view costs the
+// kernels registers they do not have to spare.  KEEP = false forms the row
+// address from the arguments at each load instead of keeping it (fewer live
+// registers in the H=128 kernel; the H=64 kernel does better keeping it).
+template <bool GEN, bool KEEP = true>
 struct TokenTable {
+  int t;
   const int32_t* row1;
   const int32_t* row2;
   int P;        // columns of the first table
@@ -222,53 +230,77 @@ struct TokenTable {
   int L1, L2;   // active columns of each table
   // the stored entry of column c (whether or not the column is active); a
   // page-table row that does not fit an int comes back as -2 (invalid)
-  __device__ __forceinline__ int raw(int c) const {
-    if (c < P) return row1[c];
+  __device__ __forceinline__ int raw(const DecodeParams& p, int c) const {
+    if constexpr (!GEN && !KEEP) return p.indices[(int64_t)t * p.index_row_stride + c];
+    if (GEN ? c < P : true) return row1[c];
     const int j = c - P;
     if (ps == 0) return row2[j];
     const int64_t r = (int64_t)row2[j / ps] * ps + j % ps;
     return (r >= 0 && r <= 0x7FFFFFFF) ? (int)r : -2;
   }
-  // column c is below its table's length
-  __device__ __forceinline__ bool live(int c) const { return c < P ? c < L1 : c - P < L2; }
+  // column c is below its table's length (callers also keep c < end(),
+  // which in the combined form already says so)
+  __device__ __forceinline__ bool live(int c) const {
+    if constexpr (!GEN) return true;
+    return c < P ? c < L1 : c - P < L2;
+  }
   // one past the last column that can be active
-  __device__ __forceinline__ int end() const { return L2 > 0 ? P + L2 : L1; }
+  __device__ __forceinline__ int end() const {
+    if constexpr (!GEN) return L1;
+    return L2 > 0 ? P + L2 : L1;
+  }
+  // column c names an SWA row
+  __device__ __forceinline__ bool swa(int c) const {
+    if constexpr (!GEN) return c < kSwaColumns;
+    return c < P;
+  }
 };
 
-__device__ __forceinline__ TokenTable token_table(const DecodeParams& p, int t) {
-  TokenTable tt;
-  tt.P = p.swa_cols;
-  tt.row1 = p.indices + (int64_t)t * p.index_row_stride;
-  tt.row2 = p.indices2 + (int64_t)t * p.index_row_stride2;
-  tt.ps = p.segmented == 2 ? p.page_size : 0;
+template <bool GEN, bool KEEP = true>
+__device__ __forceinline__ TokenTable<GEN, KEEP> token_table(const DecodeParams& p, int t) {
+  TokenTable<GEN, KEEP> tt;
+  tt.t = t;
+  tt.row1 = (GEN || KEEP) ? p.indices + (int64_t)t * p.index_row_stride : nullptr;
+  if constexpr (GEN) {
+    tt.P = p.swa_cols;
+    tt.row2 = p.indices2 + (int64_t)t * p.index_row_stride2;
+    tt.ps = p.segmented == 2 ? p.page_size : 0;
+  } else {
+    tt.P = kSwaColumns;
+    tt.row2 = nullptr;
+    tt.ps = 0;
+  }
   tt.L1 = tt.L2 = 0;
   return tt;
 }
 
-// Reads the token's length(s) into tt (clamped to the tables) and reports
-// whether they were in range.
-__device__ __forceinline__ bool token_lengths(const DecodeParams& p, int t, TokenTable& tt) {
-  if (p.segmented == 2) {
-    // visible window, then window + compressed slots
-    const int a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
-    const int tot = p.lens2 ? p.lens2[t] : p.swa_cols + p.K2;
-    tt.L1 = min(max(a, 0), p.swa_cols);
-    const int n = tot - tt.L1;
-    tt.L2 = min(max(n, 0), p.K2);
-    return a >= 0 && a <= p.swa_cols && n >= 0 && n <= p.K2;
+// The token's raw length(s), loaded early (they are used after the Q loads):
+// combined form a = topk_len; two segments a, b = the two tables' lengths;
+// page table a = window, b = window + compressed slots.
+template <bool GEN>
+__device__ __forceinline__ void token_length_loads(const DecodeParams& p, int t, int& a, int& b) {
+  if constexpr (!GEN) {
+    a = p.topk_lens ? p.topk_lens[t] : p.K;
+    b = 0;
+  } else {
+    a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
+    b = p.lens2 ? p.lens2[t] : (p.segmented == 2 ? p.swa_cols + p.K2 : p.K2);
   }
-  if (p.segmented) {
-    const int a = p.topk_lens ? p.topk_lens[t] : p.swa_cols;
-    const int b = p.lens2 ? p.lens2[t] : p.K2;
-    tt.L1 = min(max(a, 0), p.swa_cols);
-    tt.L2 = min(max(b, 0), p.K2);
-    return a >= 0 && a <= p.swa_cols && b >= 0 && b <= p.K2;
+}
+
+// Clamps the raw lengths into tt and reports whether they were in range.
+// (Combined form: L1 is the whole length.)
+template <bool GEN, bool KEEP>
+__device__ __forceinline__ bool token_lengths(const DecodeParams& p, int a, int b,
+                                              TokenTable<GEN, KEEP>& tt) {
+  if constexpr (!GEN) {
+    tt.L1 = min(max(a, 0), p.K);
+    return a >= 0 && a <= p.K;
   }
-  const int len = p.topk_lens ? p.topk_lens[t] : p.K;
-  const int l = min(max(len, 0), p.K);
-  tt.L1 = min(l, tt.P);
-  tt.L2 = max(l - tt.P, 0);
-  return len >= 0 && len <= p.K;
+  tt.L1 = min(max(a, 0), p.swa_cols);
+  const int n = p.segmented == 2 ? b - tt.L1 : b;   // compressed slots
+  tt.L2 = min(max(n, 0), p.K2);
+  return a >= 0 && a <= p.swa_cols && n >= 0 && n <= p.K2;
 }
 
 // ---------------------------------------------------------------------------
@@ -292,7 +324,7 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
   return 8 * (i >> 2) + 4 * kg + (i & 3);
 }
 
-template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT>
+template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN>
 __global__ __launch_bounds__(NW * 64, 1)
 void decode_kernel(DecodeParams p) {
   constexpr int H = NW * 32;              // one wave per 32 heads
@@ -327,8 +359,10 @@ void decode_kernel(DecodeParams p) {
   const int s = item - t * p.S;
   const int head = wave * 32 + l32;
 
-  TokenTable tt = token_table(p, t);
-  const bool lens_ok = token_lengths(p, t, tt);
+  TokenTable<GEN> tt = token_table<GEN>(p, t);
+  int len_a, len_b;
+  token_length_loads<GEN>(p, t, len_a, len_b);
+  const bool lens_ok = token_lengths<GEN>(p, len_a, len_b, tt);
   if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
   const int c_begin = s * p.split_cols;
   const int c_end = min(tt.end(), c_begin + p.split_cols);
@@ -477,9 +511,9 @@ void decode_kernel(DecodeParams p) {
       bool act = false;
       int code = 0;
       if (c < seg1 && tt.live(c)) {
-        const int r = tt.raw(c);
+        const int r = tt.raw(p, c);
         if (r != -1) {
-          const bool swa = c < tt.P;
+          const bool swa = tt.swa(c);
           const int64_t rows = swa ? p.swa_rows : p.comp_rows;
           if (r >= 0 && (int64_t)r < rows) {
             act = true;
@@ -728,7 +762,7 @@ struct BoolC {
 // rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
-template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false>
 __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   constexpr int NW = 4, H = 128, NT = 256;
   constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
@@ -769,13 +803,14 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   // waiting for the table entries does not wait for Q.
   const int c_begin = s * p.split_cols;
   const int c_cap = min(p.K, c_begin + p.split_cols);
-  TokenTable tt = token_table(p, t);
-  const bool lens_ok = token_lengths(p, t, tt);
+  TokenTable<GEN, false> tt = token_table<GEN, false>(p, t);
+  int len_a, len_b;
+  token_length_loads<GEN>(p, t, len_a, len_b);
   int rv[CPT];
   auto load_idx = [&](int seg0, int seg_hi) {
     const int cb = seg0 + threadIdx.x * CPT;
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) rv[k] = (cb + k < seg_hi) ? tt.raw(cb + k) : -1;
+    for (int k = 0; k < CPT; ++k) rv[k] = (cb + k < seg_hi) ? tt.raw(p, cb + k) : -1;
   };
   load_idx(c_begin, min(c_cap, c_begin + kSegHd));
   __builtin_amdgcn_sched_barrier(0);
@@ -796,6 +831,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 
   __builtin_amdgcn_sched_barrier(0);
+  const bool lens_ok = token_lengths<GEN>(p, len_a, len_b, tt);
   if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
   const int c_end = min(tt.end(), c_cap);
 
@@ -942,7 +978,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       const int c = cb + k;
       const int r = rv[k];
       if (r != -1 && c < seg1 && tt.live(c)) {
-        const int64_t rows = (c < tt.P) ? p.swa_rows : p.comp_rows;
+        const int64_t rows = tt.swa(c) ? p.swa_rows : p.comp_rows;
         if (r >= 0 && (int64_t)r < rows) actm |= 1u << k;
         else if (p.validate) record_error(p.err, 1, t, c);
       }
@@ -967,7 +1003,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       if ((actm >> k) & 1u) {
-        last = (cb + k < tt.P) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
+        last = tt.swa(cb + k) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
         slots[pos++] = last;
       }
     }
@@ -1256,10 +1292,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 }
 
-template <bool Q_FP8, bool KV_FP8, bool SPLIT>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
-  decode_hd_body<Q_FP8, KV_FP8, SPLIT>(p);
+  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN>(p);
 }
 
 // The row gather of decode_hd_kernel alone (BF16 rows), under its own name.
@@ -1336,25 +1372,36 @@ __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
 
+// GEN: the two-segment and page-table forms; the combined form runs the
+// plain table view.
 template <bool QF, bool KF>
 hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
-  if (p.S > 1)
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true>), grid, dim3(256), 0, stream, p);
+  const bool gen = p.segmented != 0;
+  if (p.S > 1 && gen)
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, true>), grid, dim3(256), 0, stream, p);
+  else if (p.S > 1)
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, false>), grid, dim3(256), 0, stream, p);
+  else if (gen)
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, true>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int NW, bool QF, bool KF>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
-  if (p.S > 1)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true>), grid, dim3(NW * 64), 0,
-                       stream, p);
+  const dim3 block(NW * 64);
+  const bool gen = p.segmented != 0;
+  if (p.S > 1 && gen)
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, true>), grid, block, 0, stream, p);
+  else if (p.S > 1)
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false>), grid, block, 0, stream, p);
+  else if (gen)
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false>), grid, dim3(NW * 64), 0,
-                       stream, p);
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
