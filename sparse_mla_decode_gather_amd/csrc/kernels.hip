@@ -194,6 +194,8 @@ typedef u32x2 __attribute__((address_space(1))) global_u32x2;
 __device__ __forceinline__ u32x2 load_global8(const uint8_t* row, uint32_t off) {
   return *(const global_u32x2*)(row + off);
 }
+typedef u32x4 __attribute__((address_space(1))) global_u32x4;
+typedef int32_t __attribute__((address_space(1))) global_i32;
 
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
                                              int c) {
@@ -231,11 +233,12 @@ struct TokenTable {
   // the stored entry of column c (whether or not the column is active); a
   // page-table row that does not fit an int comes back as -2 (invalid)
   __device__ __forceinline__ int raw(const DecodeParams& p, int c) const {
-    if constexpr (!GEN && !KEEP) return p.indices[(int64_t)t * p.index_row_stride + c];
-    if (GEN ? c < P : true) return row1[c];
+    if constexpr (!GEN && !KEEP)
+      return *(const global_i32*)(p.indices + (int64_t)t * p.index_row_stride + c);
+    if (GEN ? c < P : true) return *(const global_i32*)(row1 + c);
     const int j = c - P;
-    if (ps == 0) return row2[j];
-    const int64_t r = (int64_t)row2[j / ps] * ps + j % ps;
+    if (ps == 0) return *(const global_i32*)(row2 + j);
+    const int64_t r = (int64_t)*(const global_i32*)(row2 + j / ps) * ps + j % ps;
     return (r >= 0 && r <= 0x7FFFFFFF) ? (int)r : -2;
   }
   // column c is below its table's length (callers also keep c < end(),
@@ -799,8 +802,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 
   // Loads in the order their results are needed: topk_len, the first
   // segment's table entries (fetched before topk_len is known; columns past
-  // it are dropped in the compaction), then Q.  vmcnt retires in order, so
-  // waiting for the table entries does not wait for Q.
+  // it are dropped in the compaction), then Q, all through global (not flat)
+  // pointers so that LDS waits and barriers do not wait for them.  vmcnt
+  // retires in order, so the compaction's wait for the table entries does
+  // not wait for Q, and Q lands while the compaction runs.
   const int c_begin = s * p.split_cols;
   const int c_cap = min(p.K, c_begin + p.split_cols);
   TokenTable<GEN, false> tt = token_table<GEN, false>(p, t);
@@ -823,9 +828,9 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       const int d0 = kk * 16 + kg * 8;
       u32x4 v;
       if constexpr (Q_FP8)
-        v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
+        v = widen_e4m3fn_x8(load_global8((const uint8_t*)p.q + qrow, d0));
       else
-        v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
+        v = *(const global_u32x4*)((const uint16_t*)p.q + qrow + d0);
       qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -984,11 +989,15 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       }
     }
     const int cnt = __popc(actm);
-    int incl = cnt;                      // inclusive prefix over the wave
+    // exclusive prefix of cnt (<= CPT < 16) over the wave: one ballot per
+    // bit of cnt, each counted below this lane with mbcnt (no LDS trips)
+    static_assert(CPT < 16, "four ballots cover cnt");
+    int incl = cnt;
 #pragma unroll
-    for (int o2 = 1; o2 < 64; o2 <<= 1) {
-      const int y = __shfl_up(incl, o2);
-      incl += (lane >= o2) ? y : 0;
+    for (int b = 0; b < 4; ++b) {
+      const uint64_t m = __ballot((cnt >> b) & 1);
+      incl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
     }
     if (lane == 63) wave_cnt[wave] = incl;
     __syncthreads();
@@ -1054,10 +1063,11 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
                            (uint32_t)((wave_u * RPW + jj) * kRowPitch);
       lds_dma_row16(row, lane_off, dst);
     };
-    // Q has landed before the first row gather goes out: the compiler's own
-    // waits for Q count only its loads, so they would otherwise also wait
-    // for the gathers issued after Q.
-    if (!KV_FP8 && ntiles > 0) wait_vmcnt<0>();
+    // The first row gathers go out without waiting for Q: loads retire in
+    // order, so the wait for tile 0 also covers Q.  (The compiler's own
+    // waits for the last Q fragments, which count only its loads, may then
+    // also wait for some of tile 1's rows in the first S^T: a one-off cost
+    // far below Q's latency.)
 
     if constexpr (KV_FP8) {
       if (ntiles > 0) {
