@@ -1,5 +1,6 @@
 """GPU: HIP-graph capture of the decode (split kernel + combine) replays
-bit-identically to eager launches, and the gather-only measurement entry
+bit-identically to eager launches, for the combined table and for the
+two-segment and page-table forms, and the gather-only measurement entry
 point runs on the headline shape without disturbing later decodes."""
 
 import pytest
@@ -51,6 +52,66 @@ def test_graph_replays_match_eager(T, splits):
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
         assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), rep
+
+
+def _replays_match_eager(call, out, lse, what):
+    """Eager reference, then a captured graph of the same call replayed four
+    times with eager work and synchronisation in between."""
+    call(out, lse)
+    torch.cuda.synchronize()
+    ref_out, ref_lse = out.clone(), lse.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):               # warm-up off the capture
+        call(out, lse)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, lse)
+    for rep in range(4):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), (what, rep)
+        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), (what, rep)
+
+
+@pytest.mark.parametrize("form,splits", [("segments", 4), ("segments", 1),
+                                         ("paged", 8), ("paged", 1)])
+def test_graph_replays_of_the_other_table_forms(form, splits):
+    need_gpu()
+    T = 4
+    w = W.make_long_context(T, "cuda")
+    plan = L.plan_splits(T, w.H, w.K, num_splits=splits)
+    ws = L.alloc_workspace(plan, T, w.H)
+    log(f"[graph] {form} T={T} plan={plan.as_dict()}")
+    out = torch.empty((T, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    swa_len = torch.tensor([128, 100, 0, 128], dtype=torch.int32, device="cuda")
+    if form == "segments":
+        extra_len = torch.tensor([1920, 7, 1000, 0], dtype=torch.int32, device="cuda")
+
+        def call(o, l):
+            L.decode_segments(w.q, w.swa_pool, w.comp_pool, w.indices[:, :128],
+                              w.indices[:, 128:], o, swa_topk_lens=swa_len,
+                              extra_topk_lens=extra_len, out_lse=l, sinks=w.sinks,
+                              bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                              plan=plan, workspace=ws)
+    else:
+        pages = w.comp_pool.shape[0] // 64
+        g = torch.Generator().manual_seed(3)
+        bt = torch.randperm(pages, generator=g)[:T * 30].view(T, 30).int().cuda()
+        tot = swa_len + torch.tensor([1920, 64, 1, 0], dtype=torch.int32, device="cuda")
+
+        def call(o, l):
+            L.decode_paged(w.q, w.swa_pool, w.comp_pool, w.indices[:, :128], bt, 64, o,
+                           swa_topk_lens=swa_len, topk_lens=tot, out_lse=l, sinks=w.sinks,
+                           bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                           plan=plan, workspace=ws)
+    _replays_match_eager(call, out, lse, form)
 
 
 def test_gather_only_runs_on_the_headline_shape():
