@@ -199,9 +199,9 @@ def main():
                          "times (known bytes) for counter calibration")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not "
-              "supported (the sharding design is described in DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py: the decode is measured on one GPU; --gpus {args.gpus} is "
+              "not supported (tokens would shard across GPUs with no exchange, so "
+              "the per-GPU rate is the one-GPU rate)", file=sys.stderr)
         sys.exit(2)
 
     import torch

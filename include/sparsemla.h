@@ -271,8 +271,7 @@ int sparse_mla_decode_paged(const smla_decode_args* args, const smla_paged* pg,
 /* Measurement aid (not part of the method): run only the table compaction
  * and the row gather of sparse_mla_decode on the same arguments and plan,
  * with no arithmetic and no output, to give the attainable gathered-row
- * bandwidth on these exact tables (the survey's companion pure-gather
- * benchmark).  Same argument checks as sparse_mla_decode except that out,
+ * bandwidth on these exact tables (a companion pure-gather benchmark).  Same argument checks as sparse_mla_decode except that out,
  * out_lse and the workspace are not used; only H = 128 with BF16 q and
  * rows is supported (else SMLA_ERR_UNSUPPORTED_SHAPE / _DTYPE).
  * Asynchronous on "stream"; no allocation. */
