@@ -168,6 +168,11 @@ __device__ __forceinline__ void wait_vmcnt() {
 // The row address is wave-uniform: it lives in SGPRs (`row`) and each lane
 // adds its own byte offset `lane_off` (16 * lane), so issuing a row costs
 // scalar work only.
+//
+// STREAM: the load carries the non-temporal hint, for calls whose gathered
+// rows are too many to still be cached when the next call runs (see
+// kStreamingBytes below).
+template <bool STREAM = false>
 __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
                                               uint32_t lane_off,
                                               uint32_t lds_addr) {
@@ -175,16 +180,29 @@ __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
   // s_nop 4: the row address may have just been written by a VALU
   // (v_readlane / v_readfirstlane), and a VMEM read of a VALU-written SGPR
   // needs 5 wait states; s_nop 0: M0 written by SALU before LDS-DMA.
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(lane_off), "s"(row), "s"(lds_addr)
-      : "memory");
+  if constexpr (STREAM) {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2 nt\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_off), "s"(row), "s"(lds_addr)
+        : "memory");
+  } else {
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(lane_off), "s"(row), "s"(lds_addr)
+        : "memory");
+  }
 }
 
 // 8 bytes of a row through a global (not flat) pointer: row addresses are
@@ -765,7 +783,8 @@ struct BoolC {
 // rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
-template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false,
+          bool STREAM = false>
 __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   constexpr int NW = 4, H = 128, NT = 256;
   constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
@@ -1061,7 +1080,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     auto issue_row = [&](int tile, int jj, const uint8_t* row) {
       const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
                            (uint32_t)((wave_u * RPW + jj) * kRowPitch);
-      lds_dma_row16(row, lane_off, dst);
+      lds_dma_row16<STREAM>(row, lane_off, dst);
     };
     // The first row gathers go out without waiting for Q: loads retire in
     // order, so the wait for tile 0 also covers Q.  (The compiler's own
@@ -1302,16 +1321,17 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 }
 
-template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
-  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN>(p);
+  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN, STREAM>(p);
 }
 
 // The row gather of decode_hd_kernel alone (BF16 rows), under its own name.
+template <bool STREAM>
 __global__ __launch_bounds__(256, 1)
 void gather_only_kernel(DecodeParams p) {
-  decode_hd_body<false, false, false, true>(p);
+  decode_hd_body<false, false, false, true, false, STREAM>(p);
 }
 
 // ---------------------------------------------------------------------------
@@ -1382,21 +1402,43 @@ __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
 
+// Streaming rows.  A call that can gather at least this many bytes of BF16
+// rows (T x K x 1 KB) does not leave them in MI355X's 256 MB last-level
+// cache (Infinity Cache) for the next call, so its LDS-DMA row loads carry
+// the non-temporal hint.  Measured at H=128, K=2048 against the plain loads:
+// T=512 (1 GB) 3-4% faster, T=128 (256 MB) 1.5-2.5% faster, T=64 (128 MB)
+// 1.5% slower and K=512 at T=64 (32 MB) 5% slower, where back-to-back calls
+// on the same tables still find their rows cached.
+constexpr int64_t kStreamingBytes = int64_t(256) << 20;
+
+bool streaming_rows(const DecodeParams& p) {
+  return (int64_t)p.T * p.K * (kHeadDim * 2) >= kStreamingBytes;
+}
+
 // GEN: the two-segment and page-table forms; the combined form runs the
 // plain table view.
-template <bool QF, bool KF>
-hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
+template <bool QF, bool KF, bool STREAM>
+hipError_t launch_decode_hd_s(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const bool gen = p.segmented != 0;
   if (p.S > 1 && gen)
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, true, STREAM>), grid, dim3(256), 0, stream, p);
   else if (p.S > 1)
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, false, STREAM>), grid, dim3(256), 0, stream, p);
   else if (gen)
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, true>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, true, STREAM>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, false, STREAM>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// FP8 rows go through registers (no LDS-DMA), so only BF16 rows stream.
+template <bool QF, bool KF>
+hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
+  if constexpr (!KF) {
+    if (streaming_rows(p)) return launch_decode_hd_s<QF, KF, true>(p, stream);
+  }
+  return launch_decode_hd_s<QF, KF, false>(p, stream);
 }
 
 template <int NW, bool QF, bool KF>
@@ -1432,8 +1474,12 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
 
 hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream) {
   if (p.H != 128) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gather_only_kernel, dim3((unsigned)(p.T * p.S)),
-                     dim3(256), 0, stream, p);
+  if (streaming_rows(p))
+    hipLaunchKernelGGL(gather_only_kernel<true>, dim3((unsigned)(p.T * p.S)),
+                       dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(gather_only_kernel<false>, dim3((unsigned)(p.T * p.S)),
+                       dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

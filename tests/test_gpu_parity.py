@@ -344,6 +344,35 @@ def test_runs_are_bitwise_deterministic():
     assert torch.equal(la, lb)
 
 
+def test_streaming_row_loads_match_plain_loads():
+    """A call that can gather >= 256 MB of BF16 rows loads them with the
+    non-temporal hint; the same tokens in a small call use plain loads.  The
+    hint changes only cache placement, so both give identical bits."""
+    need_gpu()
+    T, K = 128, 2048                    # 128 x 2048 x 1 KB = 256 MB
+    g = np.random.default_rng(11)
+    idx = np.concatenate([
+        np.stack([g.choice(600, 128, replace=False) for _ in range(T)]),
+        np.stack([g.choice(4000, K - 128, replace=False) for _ in range(T)])],
+        axis=1)
+    lens = g.integers(1, K + 1, size=T)
+    w = custom(idx, lens, swa_rows=600, comp_rows=4000, seed=21)
+    log(f"[parity] streaming vs plain loads: T={T} K={K} and T=8")
+    big, lbig = run_decode(w, plan=L.plan_splits(T, 128, K, num_splits=1))
+    n = 8
+    small = W.Workload(
+        name="custom8", T=n, H=w.H, K=K, q=w.q[:n].contiguous(), q_dtype=w.q_dtype,
+        swa_pool=w.swa_pool, comp_pool=w.comp_pool, kv_dtype=w.kv_dtype,
+        indices=w.indices[:n].contiguous(), topk_lens=w.topk_lens[:n].contiguous(),
+        seq_lens=w.seq_lens[:n].contiguous(), cum_seq_lens_q=None, sinks=w.sinks,
+        bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, lse_scale=w.lse_scale)
+    out, lse = run_decode(small, plan=L.plan_splits(n, 128, K, num_splits=1))
+    assert torch.equal(out.view(torch.int16), big[:n].view(torch.int16))
+    assert torch.equal(lse, lbig[:n])
+    check(w, tokens=range(0, T, 16), plan=L.plan_splits(T, 128, K, num_splits=1),
+          what="streaming loads vs oracle")
+
+
 def test_indices_past_topk_len_are_never_read():
     """Columns at or beyond topk_len hold indices far outside both pools;
     they must not be dereferenced (the result equals the table with those
