@@ -383,9 +383,16 @@ void decode_kernel(DecodeParams p) {
   TokenTable<GEN> tt = token_table<GEN>(p, t);
   int len_a, len_b;
   token_length_loads<GEN>(p, t, len_a, len_b);
+  // The first compaction pass's table entries go out with the lengths and
+  // before Q, so that their latency overlaps Q's instead of following it
+  // (columns past the token's length are loaded too and dropped in the
+  // compaction).
+  const int c_begin = s * p.split_cols;
+  int r_first = -1;
+  if (c_begin + (int)threadIdx.x < min(p.K, c_begin + p.split_cols))
+    r_first = tt.raw(p, c_begin + threadIdx.x);
   const bool lens_ok = token_lengths<GEN>(p, len_a, len_b, tt);
   if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
-  const int c_begin = s * p.split_cols;
   const int c_end = min(tt.end(), c_begin + p.split_cols);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds head `head`,
@@ -532,7 +539,7 @@ void decode_kernel(DecodeParams p) {
       bool act = false;
       int code = 0;
       if (c < seg1 && tt.live(c)) {
-        const int r = tt.raw(p, c);
+        const int r = (c0 == c_begin) ? r_first : tt.raw(p, c);
         if (r != -1) {
           const bool swa = tt.swa(c);
           const int64_t rows = swa ? p.swa_rows : p.comp_rows;
@@ -993,7 +1000,14 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     // Thread i takes CPT consecutive columns; all its index loads are in
     // flight together.  Slot order is column order.
     __syncthreads();   // the previous segment no longer reads slots[] / tiles
-    if (!first_seg) load_idx(seg0, seg1);
+    if (!first_seg) {
+      // Later segments (and restarts) reload the table and wait for it here,
+      // where nothing else is in flight.  Without this wait the compiler
+      // would have to wait for every load at the merge below, so the first
+      // segment's compaction would also wait for all of Q.
+      load_idx(seg0, seg1);
+      wait_vmcnt<0>();
+    }
     first_seg = false;
     const int cb = seg0 + threadIdx.x * CPT;
     uint32_t actm = 0;
