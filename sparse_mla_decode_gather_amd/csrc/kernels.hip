@@ -1355,7 +1355,14 @@ void gather_only_kernel(DecodeParams p) {
 __global__ __launch_bounds__(256)
 void combine_kernel(CombineParams p) {
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + (threadIdx.x >> 6);
+  // The same XCD-aware mapping as the split kernels: XCD x takes the x-th
+  // contiguous range of blocks, i.e. about the same tokens whose partials
+  // it wrote, so they are read from its own L2.
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int q8 = nblk >> 3, r8 = nblk & 7;
+  const int blk = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
+  const int item = blk * 4 + (threadIdx.x >> 6);
   if (item >= p.T * p.H) return;
   const int h = item % p.H;
   const float* ml = p.mid_lse + (size_t)item * p.stride;
