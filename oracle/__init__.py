@@ -14,6 +14,8 @@ from the method's definition as the FlashInfer and vLLM pages state it:
   base-2 LSE), its split form and the LSE combine.
 * ``brute``    - a second, independent formulation (multiset of pool rows,
   pure-Python loops, optional mpmath arithmetic) used to pin the first.
+* ``index_builder`` - the combined index table built from decode metadata
+  (SWA rows + local compressed positions through a block table).
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by tests in ``tests/test_oracle_*.py`` except where a
@@ -28,6 +30,7 @@ from .sparse_mla import (SWA_COLUMNS, active_slots, active_slots_segments,
                          split_partials, combine, split_columns)
 from .brute import (brute_force_decode, brute_force_decode_segments,
                     brute_force_decode_paged)
+from .index_builder import build_combined_indices
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "decode_bits", "round_to_bf16",
@@ -36,4 +39,5 @@ __all__ = [
     "sparse_mla_decode_segments", "sparse_mla_decode_paged", "split_partials",
     "combine", "split_columns", "brute_force_decode",
     "brute_force_decode_segments", "brute_force_decode_paged",
+    "build_combined_indices",
 ]
