@@ -28,7 +28,9 @@ plainest the rest supports):
   * Compressed columns at or past the token's compressed length are -1; the
     token's length is ``W + n2`` with ``n2`` the compressed length clamped to
     [0, K2] (``K2`` when no lengths are given), ``W`` the SWA width.
-  * A token marked invalid (padding) gets an all -1 row and length 0.
+  * A token marked invalid (padding) gets an all -1 row and length 0, and so
+    does (local form) a token whose request index lies outside the block
+    table; the latter is reported with column -1.
 """
 
 from __future__ import annotations
@@ -63,11 +65,14 @@ def build_combined_indices(swa_indices: np.ndarray, comp_indices: np.ndarray, *,
     for t in range(T):
         if valid_tokens is not None and not valid_tokens[t]:
             continue
+        req = t if token_to_req is None else int(token_to_req[t])
+        if local and K2 > 0 and not 0 <= req < block_tables.shape[0]:
+            bad.append((t, -1))
+            continue
         n2 = K2 if comp_topk_lens is None else int(comp_topk_lens[t])
         n2 = max(0, min(n2, K2))
         lens[t] = W + n2
         out[t, :W] = swa[t]
-        req = t if token_to_req is None else int(token_to_req[t])
         for j in range(n2):
             p = int(comp[t, j])
             if p < 0:

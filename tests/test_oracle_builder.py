@@ -148,3 +148,13 @@ def test_invalid_tokens_are_empty_and_decode_to_the_sink_only_result():
     assert (r["out"][1] == 0).all()
     np.testing.assert_allclose(r["lse"][1], sinks.astype(np.float64) / np.log(2),
                                rtol=1e-6)
+
+
+def test_tokens_of_requests_outside_the_block_table_are_empty_and_reported():
+    bt = np.array([[1, 2]], dtype=np.int32)
+    idx, lens, bad = build_combined_indices(
+        np.array([[4], [5], [6]]), np.array([[0], [1], [2]]), local=True, page_size=2,
+        block_tables=bt, token_to_req=np.array([0, 1, -1]))
+    assert idx.tolist() == [[4, 2], [-1, -1], [-1, -1]]
+    assert lens.tolist() == [2, 0, 0]
+    assert bad == [(1, -1), (2, -1)]
