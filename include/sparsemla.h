@@ -268,6 +268,66 @@ typedef struct smla_paged {
 int sparse_mla_decode_paged(const smla_decode_args* args, const smla_paged* pg,
                             const smla_plan* plan, smla_stream_t stream);
 
+/* Combined index table from decode metadata: the step before the decode in
+ * vLLM's DeepSeek-V4 FlashInfer attention
+ * ("DeepseekV4FlashInferMLAAttention._build_sparse_index_metadata"), whose
+ * result is the "sparse_indices" / "sparse_topk_lens" pair of FlashInfer
+ * "trtllm_batch_decode_sparse_mla_dsv4".  Row t of out_indices is the
+ * token's SWA row followed by its compressed entries:
+ *   out[t][c]             = swa_indices[t][c]         for c < swa_width,
+ *   out[t][swa_width + j] = compressed entry j, translated, for j < n2(t),
+ *                           and -1 for n2(t) <= j < comp_width,
+ * with n2(t) = comp_topk_lens[t] clamped to [0, comp_width] (comp_width when
+ * NULL) and out_topk_lens[t] = swa_width + n2(t).  A negative entry gives
+ * -1.  With comp_local != 0 an entry is a position p within the token's
+ * request (the ratio-4 top-k positions) and becomes, by the canonical page
+ * expansion of the FlashInfer page ("hca_sparse_indices_format"),
+ *   block_tables[req][p / page_size] * page_size + p % page_size,
+ * page_size being the compressed rows per block (the KV block size divided
+ * by the compress ratio, as vLLM computes compressed_block_size) and req =
+ * token_to_req[t] (NULL: t); otherwise it is a global row and is copied
+ * (ratio 128, with "c128a_decode_topk_lens" as comp_topk_lens).  A position
+ * whose page index is >= max_blocks, whose page ID is negative or whose row
+ * exceeds INT32_MAX gives -1.  A token with valid_tokens[t] == 0, or (local
+ * form) a request index outside [0, num_requests), gets an all -1 row and
+ * length 0.  If err is not NULL it is cleared by the call and receives the
+ * first untranslatable entry (SMLA_DEVERR_INDEX_RANGE, token, column; column
+ * -1 for a bad request index); read it with sparse_mla_get_device_error.
+ * Device pointers; the caller owns them. */
+typedef struct smla_build_args {
+  int32_t T;                       /* tokens, >= 0 */
+  int32_t swa_width;               /* >= 0 (128 on the pages) */
+  int32_t comp_width;              /* >= 0; swa_width + comp_width >= 1 */
+  int32_t comp_local;              /* 1: request-local positions, 0: global rows */
+  const int32_t* swa_indices;      /* [T, swa_row_stride] (NULL iff swa_width == 0) */
+  int64_t swa_row_stride;          /* elements; 0 means swa_width */
+  const int32_t* comp_indices;     /* [T, comp_row_stride] (NULL iff comp_width == 0) */
+  int64_t comp_row_stride;         /* elements; 0 means comp_width */
+  const int32_t* comp_topk_lens;   /* [T] or NULL */
+  const int32_t* block_tables;     /* [num_requests, block_table_stride] page IDs
+                                      (local form only) */
+  int64_t block_table_stride;      /* elements; 0 means max_blocks */
+  int32_t max_blocks;              /* >= 1 (local form) */
+  int32_t page_size;               /* compressed rows per block, >= 1 (local form) */
+  int32_t num_requests;            /* >= 1 (local form) */
+  int32_t reserved;
+  const int32_t* token_to_req;     /* [T] or NULL */
+  const int32_t* valid_tokens;     /* [T] (0 = padding token) or NULL */
+  int32_t* out_indices;            /* [T, out_row_stride] */
+  int64_t out_row_stride;          /* elements; 0 means swa_width + comp_width */
+  int32_t* out_topk_lens;          /* [T] */
+  int32_t* err;                    /* 16-byte device error block, or NULL */
+} smla_build_args;
+
+/* Build the combined table (see smla_build_args).  Returns
+ * SMLA_ERR_INVALID_ARG for a NULL args, negative sizes, a zero total width,
+ * a missing table for a non-zero width, a missing output, a row stride below
+ * its width, or (local form) a missing block table or max_blocks, page_size
+ * or num_requests below 1; SMLA_ERR_MISALIGNED for a pointer that is not
+ * 4-byte aligned.  T = 0 does nothing.  Asynchronous on "stream", no
+ * allocation, graph capturable (the error block is cleared by a kernel). */
+int sparse_mla_build_indices(const smla_build_args* args, smla_stream_t stream);
+
 /* Measurement aid (not part of the method): run only the table compaction
  * and the row gather of sparse_mla_decode on the same arguments and plan,
  * with no arithmetic and no output, to give the attainable gathered-row

@@ -369,6 +369,58 @@ int sparse_mla_gather_only(const smla_decode_args* a, const smla_plan* plan,
   return SMLA_OK;
 }
 
+int sparse_mla_build_indices(const smla_build_args* a, smla_stream_t stream_handle) {
+  if (!a) return SMLA_ERR_INVALID_ARG;
+  if (a->T < 0 || a->swa_width < 0 || a->comp_width < 0) return SMLA_ERR_INVALID_ARG;
+  const int64_t K = (int64_t)a->swa_width + a->comp_width;
+  if (K < 1 || K > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
+  if (a->T == 0) return SMLA_OK;
+  const int64_t s1 = a->swa_row_stride == 0 ? a->swa_width : a->swa_row_stride;
+  const int64_t s2 = a->comp_row_stride == 0 ? a->comp_width : a->comp_row_stride;
+  const int64_t so = a->out_row_stride == 0 ? K : a->out_row_stride;
+  if ((a->swa_width > 0 && (!a->swa_indices || s1 < a->swa_width)) ||
+      (a->comp_width > 0 && (!a->comp_indices || s2 < a->comp_width)) ||
+      !a->out_indices || !a->out_topk_lens || so < K)
+    return SMLA_ERR_INVALID_ARG;
+  const bool local = a->comp_local != 0;
+  const int64_t sb = a->block_table_stride == 0 ? a->max_blocks : a->block_table_stride;
+  if (local && a->comp_width > 0 &&
+      (!a->block_tables || a->max_blocks < 1 || a->page_size < 1 ||
+       a->num_requests < 1 || sb < a->max_blocks))
+    return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)a->T * ((K + 255) / 256) > INT_MAX) return SMLA_ERR_INVALID_ARG;
+  const void* ptrs[] = {a->swa_indices, a->comp_indices, a->comp_topk_lens,
+                        a->block_tables, a->token_to_req, a->valid_tokens,
+                        a->out_indices, a->out_topk_lens, a->err};
+  for (const void* q : ptrs)
+    if (q && !aligned(q, 4)) return SMLA_ERR_MISALIGNED;
+  smla::BuildParams p{};
+  p.swa = a->swa_indices;
+  p.swa_stride = s1;
+  p.comp = a->comp_indices;
+  p.comp_stride = s2;
+  p.comp_lens = a->comp_topk_lens;
+  p.block_tables = a->block_tables;
+  p.bt_stride = sb;
+  p.token_to_req = a->token_to_req;
+  p.valid = a->valid_tokens;
+  p.out = a->out_indices;
+  p.out_stride = so;
+  p.out_lens = a->out_topk_lens;
+  p.err = a->err;
+  p.T = a->T;
+  p.W = a->swa_width;
+  p.K2 = a->comp_width;
+  p.local = (local && a->comp_width > 0) ? 1 : 0;
+  p.max_blocks = a->max_blocks;
+  p.page_size = a->page_size;
+  p.num_requests = a->num_requests;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_handle);
+  if (p.err && smla::launch_clear_error(p.err, stream) != hipSuccess) return SMLA_ERR_HIP;
+  if (smla::launch_build_indices(p, stream) != hipSuccess) return SMLA_ERR_HIP;
+  return SMLA_OK;
+}
+
 int sparse_mla_combine(const void* mid_out, const float* mid_lse, int T, int H,
                        int S, int split_stride, const float* sinks,
                        float lse_scale, void* out, float* out_lse,

@@ -61,11 +61,32 @@ struct CombineParams {
   int32_t T, H, S, stride;
 };
 
+// The combined-table builder, resolved on the host.
+struct BuildParams {
+  const int32_t* swa;            // [T, swa_stride] or null (W == 0)
+  int64_t swa_stride;
+  const int32_t* comp;           // [T, comp_stride] or null (K2 == 0)
+  int64_t comp_stride;
+  const int32_t* comp_lens;      // [T] or null
+  const int32_t* block_tables;   // [num_requests, bt_stride] (local only)
+  int64_t bt_stride;
+  const int32_t* token_to_req;   // [T] or null
+  const int32_t* valid;          // [T] or null
+  int32_t* out;                  // [T, out_stride]
+  int64_t out_stride;
+  int32_t* out_lens;             // [T]
+  int32_t* err;                  // error block or null
+  int32_t T, W, K2;
+  int32_t local;
+  int32_t max_blocks, page_size, num_requests;
+};
+
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // The H=128 BF16 gather without arithmetic or output (measurement aid).
 hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
+hipError_t launch_build_indices(const BuildParams& p, hipStream_t stream);
 
 }  // namespace smla

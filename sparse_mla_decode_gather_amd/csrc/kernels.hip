@@ -1419,6 +1419,59 @@ void combine_kernel(CombineParams p) {
     p.out_lse[item] = (W > 0.f) ? p.lse_scale * (L + fast_log2(W)) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// combined-table builder: one thread per output column
+// ---------------------------------------------------------------------------
+//
+// The step before the decode (vLLM DeepseekV4FlashInferMLAAttention,
+// _build_sparse_index_metadata): token t's row of the combined table is its
+// SWA row followed by its compressed entries, a request-local position p
+// becoming row block_tables[req][p / page_size] * page_size + p % page_size
+// (the canonical page expansion of FlashInfer's hca_sparse_indices_format)
+// and a global row being copied.  Columns past the token's compressed
+// length are -1, its length is W + that length; a padding token (or one
+// whose request index is out of range) gets an all -1 row and length 0.
+// An entry that cannot be translated becomes -1 and is recorded in err.
+
+__global__ __launch_bounds__(256)
+void build_indices_kernel(BuildParams p) {
+  const int K = p.W + p.K2;
+  const int per_row = (K + 255) / 256;
+  const int t = blockIdx.x / per_row;
+  const int c = (blockIdx.x - t * per_row) * 256 + threadIdx.x;
+  bool valid = p.valid == nullptr || p.valid[t] != 0;
+  const int req = p.token_to_req ? p.token_to_req[t] : t;
+  if (valid && p.local && (req < 0 || req >= p.num_requests)) {
+    valid = false;
+    if (p.err && c == 0) record_error(p.err, 1, t, -1);
+  }
+  const int n2 = p.comp_lens ? min(max(p.comp_lens[t], 0), p.K2) : p.K2;
+  if (c == 0) p.out_lens[t] = valid ? p.W + n2 : 0;
+  if (c >= K) return;
+  int v = -1;
+  if (valid) {
+    if (c < p.W) {
+      v = p.swa[(int64_t)t * p.swa_stride + c];
+    } else if (c - p.W < n2) {
+      const int e = p.comp[(int64_t)t * p.comp_stride + (c - p.W)];
+      if (e >= 0 && !p.local) {
+        v = e;
+      } else if (e >= 0) {
+        const int blk = e / p.page_size;
+        bool bad = blk >= p.max_blocks;
+        if (!bad) {
+          const int page = p.block_tables[(int64_t)req * p.bt_stride + blk];
+          const int64_t row = (int64_t)page * p.page_size + e % p.page_size;
+          bad = page < 0 || row > 0x7FFFFFFF;
+          if (!bad) v = (int)row;
+        }
+        if (bad && p.err) record_error(p.err, 1, t, c);
+      }
+    }
+  }
+  p.out[(int64_t)t * p.out_stride + c] = v;
+}
+
 __global__ void clear_error_kernel(int32_t* err) {
   if (threadIdx.x < 4) err[threadIdx.x] = (threadIdx.x == 0) ? 0 : -1;
 }
@@ -1513,6 +1566,12 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
 
 hipError_t launch_clear_error(int32_t* err, hipStream_t stream) {
   hipLaunchKernelGGL(clear_error_kernel, dim3(1), dim3(64), 0, stream, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_indices(const BuildParams& p, hipStream_t stream) {
+  const int64_t blocks = (int64_t)p.T * ((p.W + p.K2 + 255) / 256);
+  hipLaunchKernelGGL(build_indices_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

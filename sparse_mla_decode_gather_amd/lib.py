@@ -92,6 +92,23 @@ class Paged(ctypes.Structure):
     ]
 
 
+class BuildArgs(ctypes.Structure):
+    """smla_build_args: decode metadata -> combined table."""
+    _fields_ = [
+        ("T", ctypes.c_int32), ("swa_width", ctypes.c_int32),
+        ("comp_width", ctypes.c_int32), ("comp_local", ctypes.c_int32),
+        ("swa_indices", ctypes.c_void_p), ("swa_row_stride", ctypes.c_int64),
+        ("comp_indices", ctypes.c_void_p), ("comp_row_stride", ctypes.c_int64),
+        ("comp_topk_lens", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p), ("block_table_stride", ctypes.c_int64),
+        ("max_blocks", ctypes.c_int32), ("page_size", ctypes.c_int32),
+        ("num_requests", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("token_to_req", ctypes.c_void_p), ("valid_tokens", ctypes.c_void_p),
+        ("out_indices", ctypes.c_void_p), ("out_row_stride", ctypes.c_int64),
+        ("out_topk_lens", ctypes.c_void_p), ("err", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -126,6 +143,8 @@ def load() -> ctypes.CDLL:
         ctypes.POINTER(DecodeArgs), ctypes.POINTER(Paged), ctypes.POINTER(Plan),
         ctypes.c_void_p]
     lib.sparse_mla_decode_paged.restype = ctypes.c_int
+    lib.sparse_mla_build_indices.argtypes = [ctypes.POINTER(BuildArgs), ctypes.c_void_p]
+    lib.sparse_mla_build_indices.restype = ctypes.c_int
     lib.sparse_mla_gather_only.argtypes = [ctypes.POINTER(DecodeArgs),
                                            ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_gather_only.restype = ctypes.c_int
@@ -383,6 +402,63 @@ def decode_segments(q, swa_pool, compressed_pool, swa_indices, extra_indices, ou
                                              ctypes.byref(plan), _stream(stream)),
            "sparse_mla_decode_segments")
     return plan
+
+
+def build_args(T: int, swa_indices, comp_indices, *, comp_local: bool,
+               comp_topk_lens=None, block_tables=None, page_size: int = 0,
+               token_to_req=None, valid_tokens=None, out=None, out_topk_lens=None,
+               err=None) -> BuildArgs:
+    """Fill smla_build_args from int32 tensors (argument marshalling only)."""
+    b = BuildArgs()
+    b.T = int(T)
+    b.swa_width = 0 if swa_indices is None else int(swa_indices.shape[1])
+    b.comp_width = 0 if comp_indices is None else int(comp_indices.shape[1])
+    b.comp_local = 1 if comp_local else 0
+    b.swa_indices = _ptr(swa_indices)
+    b.swa_row_stride = 0 if swa_indices is None else int(swa_indices.stride(0))
+    b.comp_indices = _ptr(comp_indices)
+    b.comp_row_stride = 0 if comp_indices is None else int(comp_indices.stride(0))
+    b.comp_topk_lens = _ptr(comp_topk_lens)
+    b.block_tables = _ptr(block_tables)
+    b.block_table_stride = 0 if block_tables is None else int(block_tables.stride(0))
+    b.max_blocks = 0 if block_tables is None else int(block_tables.shape[1])
+    b.page_size = int(page_size)
+    b.num_requests = 0 if block_tables is None else int(block_tables.shape[0])
+    b.token_to_req = _ptr(token_to_req)
+    b.valid_tokens = _ptr(valid_tokens)
+    b.out_indices = _ptr(out)
+    b.out_row_stride = 0 if out is None else int(out.stride(0))
+    b.out_topk_lens = _ptr(out_topk_lens)
+    b.err = _ptr(err)
+    return b
+
+
+def build_indices(swa_indices, comp_indices, *, comp_local: bool,
+                  comp_topk_lens=None, block_tables=None, page_size: int = 0,
+                  token_to_req=None, valid_tokens=None, out=None,
+                  out_topk_lens=None, err=None, stream=None):
+    """sparse_mla_build_indices: the combined table [T, W + K2] and its
+    lengths [T] (int32, allocated here unless given) from the token's SWA
+    rows and compressed entries (request-local positions through
+    ``block_tables`` with ``page_size`` rows per block when ``comp_local``,
+    else global rows).  ``err`` (int32[4] on the device, optional) receives
+    the first untranslatable entry."""
+    ref = swa_indices if swa_indices is not None else comp_indices
+    T = int(ref.shape[0])
+    K = (0 if swa_indices is None else int(swa_indices.shape[1])) + \
+        (0 if comp_indices is None else int(comp_indices.shape[1]))
+    if out is None:
+        out = torch.empty((T, K), dtype=torch.int32, device=ref.device)
+    if out_topk_lens is None:
+        out_topk_lens = torch.empty((T,), dtype=torch.int32, device=ref.device)
+    b = build_args(T, swa_indices, comp_indices, comp_local=comp_local,
+                   comp_topk_lens=comp_topk_lens, block_tables=block_tables,
+                   page_size=page_size, token_to_req=token_to_req,
+                   valid_tokens=valid_tokens, out=out, out_topk_lens=out_topk_lens,
+                   err=err)
+    _check(load().sparse_mla_build_indices(ctypes.byref(b), _stream(stream)),
+           "sparse_mla_build_indices")
+    return out, out_topk_lens
 
 
 def gather_only(q, swa_pool, compressed_pool, indices, *, topk_lens=None,

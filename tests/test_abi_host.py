@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported(so):
         "sparse_mla_plan_splits", "sparse_mla_workspace_size",
         "sparse_mla_workspace_layout", "sparse_mla_decode",
         "sparse_mla_gather_only", "sparse_mla_decode_segments",
-        "sparse_mla_decode_paged",
+        "sparse_mla_decode_paged", "sparse_mla_build_indices",
         "sparse_mla_combine", "sparse_mla_get_device_error",
         "sparse_mla_status_string"}
     for n in names:
@@ -426,3 +426,78 @@ def test_paged_rejects(so, change, code):
     elif change == "block_misaligned":
         g.block_tables = DUMMY + 2
     assert call_paged(so, a, g) == code
+
+
+# ---------------------------------------------------------------------------
+# sparse_mla_build_indices
+# ---------------------------------------------------------------------------
+
+def good_build(T=4, W=128, K2=64, local=True):
+    b = L.BuildArgs()
+    b.T, b.swa_width, b.comp_width, b.comp_local = T, W, K2, 1 if local else 0
+    b.swa_indices = DUMMY if W else None
+    b.comp_indices = DUMMY + 4096 if K2 else None
+    b.block_tables = DUMMY + 8192 if local else None
+    b.max_blocks, b.page_size, b.num_requests = 8, 16, T
+    b.out_indices = DUMMY + 16384
+    b.out_topk_lens = DUMMY + 32768
+    return b
+
+
+def test_build_null_args_and_empty_batch(so):
+    assert so.sparse_mla_build_indices(None, None) == 1
+    b = good_build(T=0)
+    b.out_indices = b.out_topk_lens = None     # never touched for T = 0
+    b.swa_indices = b.comp_indices = b.block_tables = None
+    assert so.sparse_mla_build_indices(ctypes.byref(b), None) == 0
+
+
+@pytest.mark.parametrize("change,code", [
+    ("neg_T", 1), ("neg_width", 1), ("neg_comp", 1), ("zero_width", 1),
+    ("no_swa", 1), ("no_comp", 1), ("no_out", 1), ("no_lens", 1),
+    ("swa_stride", 1), ("comp_stride", 1), ("out_stride", 1),
+    ("no_block_table", 1), ("max_blocks", 1), ("page_size", 1), ("num_requests", 1),
+    ("block_stride", 1), ("misaligned_out", 5), ("misaligned_err", 5),
+    ("misaligned_req", 5),
+])
+def test_build_rejects(so, change, code):
+    b = good_build()
+    if change == "neg_T":
+        b.T = -1
+    elif change == "neg_width":
+        b.swa_width = -1
+    elif change == "neg_comp":
+        b.comp_width = -2
+    elif change == "zero_width":
+        b.swa_width = b.comp_width = 0
+    elif change == "no_swa":
+        b.swa_indices = None
+    elif change == "no_comp":
+        b.comp_indices = None
+    elif change == "no_out":
+        b.out_indices = None
+    elif change == "no_lens":
+        b.out_topk_lens = None
+    elif change == "swa_stride":
+        b.swa_row_stride = 127
+    elif change == "comp_stride":
+        b.comp_row_stride = 63
+    elif change == "out_stride":
+        b.out_row_stride = 191
+    elif change == "no_block_table":
+        b.block_tables = None
+    elif change == "max_blocks":
+        b.max_blocks = 0
+    elif change == "page_size":
+        b.page_size = 0
+    elif change == "num_requests":
+        b.num_requests = 0
+    elif change == "block_stride":
+        b.block_table_stride = 7
+    elif change == "misaligned_out":
+        b.out_indices = DUMMY + 2
+    elif change == "misaligned_err":
+        b.err = DUMMY + 1
+    elif change == "misaligned_req":
+        b.token_to_req = DUMMY + 3
+    assert so.sparse_mla_build_indices(ctypes.byref(b), None) == code
