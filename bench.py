@@ -18,7 +18,9 @@ form (sparse_mla_decode_segments with a 128-column SWA table and a
 1920-column compressed table), the rate of the page-table form
 (sparse_mla_decode_paged: the same 128 window rows plus 30 random pages of
 64 consecutive compressed rows per token; same gathered bytes, page-local
-rows), a cold-cache rate (a 1 GiB write between
+rows), the combined-table builder (sparse_mla_build_indices) timed on the
+same tables expressed as request-local positions and a 64-row block table
+(it must rebuild them exactly), a cold-cache rate (a 1 GiB write between
 launches evicts L2 and MALL), and with --sweep the per-T numbers for
 T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
 back-to-back launches.
@@ -269,6 +271,28 @@ def main():
     for _ in range(4):
         pper += time_launches(paged_step, 8, 2, stream)[1]
         cper2 += time_launches(step, 8, 2, stream)[1]
+    # combined-table builder at the same shape: each request's compressed
+    # rows expressed as positions in its own region, translated through a
+    # block table of the region's 64-row pages, rebuild the same table
+    region_rows = w.comp_pool.shape[0] // T
+    req_base = (torch.arange(T, device="cuda", dtype=torch.int32) * region_rows)[:, None]
+    comp_tab = w.indices[:, 128:]
+    local_pos = torch.where(comp_tab >= 0, comp_tab - req_base, comp_tab).contiguous()
+    bpr = region_rows // 64
+    btab = (torch.arange(T * bpr, device="cuda", dtype=torch.int32).view(T, bpr)).contiguous()
+    comp_lens = (w.topk_lens - 128).clamp(min=0).int()
+    b_out = torch.empty_like(w.indices)
+    b_lens = torch.empty_like(w.topk_lens)
+
+    def build_step():
+        lib.build_indices(swa_tab, local_pos, comp_local=True, comp_topk_lens=comp_lens,
+                          block_tables=btab, page_size=64, out=b_out,
+                          out_topk_lens=b_lens)
+    # a few-microsecond kernel: timed as HIP-graph replays, so that the
+    # Python argument marshalling between launches is not counted
+    build_ms = time_graph(build_step, launches=20, replays=5)
+    build_bytes = (2 * w.indices.numel() + btab.numel() + 2 * T) * 4
+    build_ok = bool(torch.equal(b_out, w.indices) and torch.equal(b_lens, w.topk_lens))
     cold_ms = time_cold(step, 10, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
@@ -318,6 +342,12 @@ def main():
         "paged_vs_combined": round((sum(cper2) / len(cper2)) / (sum(pper) / len(pper)), 4),
         "plan": plan.as_dict(),
         "roofline": roofline,
+        "build_indices": {"us": round(build_ms * 1e3, 2),
+                          "GBps": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
+                          "bytes": build_bytes,
+                          "hbm_frac": round(build_bytes / (build_ms * 1e-3) / 1e9
+                                            / HBM_PEAK_GBPS, 4),
+                          "rebuilds_the_table": build_ok},
     }
     if args.sweep:
         sweep = {}

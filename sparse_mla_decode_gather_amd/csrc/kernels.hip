@@ -1420,7 +1420,7 @@ void combine_kernel(CombineParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// combined-table builder: one thread per output column
+// combined-table builder: four output columns per thread
 // ---------------------------------------------------------------------------
 //
 // The step before the decode (vLLM DeepseekV4FlashInferMLAAttention,
@@ -1433,43 +1433,60 @@ void combine_kernel(CombineParams p) {
 // whose request index is out of range) gets an all -1 row and length 0.
 // An entry that cannot be translated becomes -1 and is recorded in err.
 
+constexpr int kBuildCols = 4;   // columns per thread, 256 apart (coalesced)
+
 __global__ __launch_bounds__(256)
 void build_indices_kernel(BuildParams p) {
   const int K = p.W + p.K2;
-  const int per_row = (K + 255) / 256;
+  const int per_row = (K + 256 * kBuildCols - 1) / (256 * kBuildCols);
   const int t = blockIdx.x / per_row;
-  const int c = (blockIdx.x - t * per_row) * 256 + threadIdx.x;
-  bool valid = p.valid == nullptr || p.valid[t] != 0;
+  const int c0 = (blockIdx.x - t * per_row) * (256 * kBuildCols) + threadIdx.x;
+  // the token's flags and length and this thread's entries are independent
+  // loads, issued together; only the block-table lookups depend on them
+  const int valid_raw = p.valid ? p.valid[t] : 1;
   const int req = p.token_to_req ? p.token_to_req[t] : t;
+  const int len_raw = p.comp_lens ? p.comp_lens[t] : p.K2;
+  int e[kBuildCols];
+#pragma unroll
+  for (int k = 0; k < kBuildCols; ++k) {
+    const int c = c0 + 256 * k;
+    e[k] = -1;
+    if (c < p.W) e[k] = p.swa[(int64_t)t * p.swa_stride + c];
+    else if (c < K) e[k] = p.comp[(int64_t)t * p.comp_stride + (c - p.W)];
+  }
+  bool valid = valid_raw != 0;
   if (valid && p.local && (req < 0 || req >= p.num_requests)) {
     valid = false;
-    if (p.err && c == 0) record_error(p.err, 1, t, -1);
+    if (p.err && c0 == 0) record_error(p.err, 1, t, -1);
   }
-  const int n2 = p.comp_lens ? min(max(p.comp_lens[t], 0), p.K2) : p.K2;
-  if (c == 0) p.out_lens[t] = valid ? p.W + n2 : 0;
-  if (c >= K) return;
-  int v = -1;
-  if (valid) {
-    if (c < p.W) {
-      v = p.swa[(int64_t)t * p.swa_stride + c];
-    } else if (c - p.W < n2) {
-      const int e = p.comp[(int64_t)t * p.comp_stride + (c - p.W)];
-      if (e >= 0 && !p.local) {
-        v = e;
-      } else if (e >= 0) {
-        const int blk = e / p.page_size;
-        bool bad = blk >= p.max_blocks;
-        if (!bad) {
-          const int page = p.block_tables[(int64_t)req * p.bt_stride + blk];
-          const int64_t row = (int64_t)page * p.page_size + e % p.page_size;
-          bad = page < 0 || row > 0x7FFFFFFF;
-          if (!bad) v = (int)row;
+  const int n2 = min(max(len_raw, 0), p.K2);
+  if (c0 == 0) p.out_lens[t] = valid ? p.W + n2 : 0;
+#pragma unroll
+  for (int k = 0; k < kBuildCols; ++k) {
+    const int c = c0 + 256 * k;
+    if (c >= K) break;
+    int v = -1;
+    if (valid) {
+      if (c < p.W) {
+        v = e[k];
+      } else if (c - p.W < n2 && e[k] >= 0) {
+        if (!p.local) {
+          v = e[k];
+        } else {
+          const int blk = e[k] / p.page_size;
+          bool bad = blk >= p.max_blocks;
+          if (!bad) {
+            const int page = p.block_tables[(int64_t)req * p.bt_stride + blk];
+            const int64_t row = (int64_t)page * p.page_size + e[k] % p.page_size;
+            bad = page < 0 || row > 0x7FFFFFFF;
+            if (!bad) v = (int)row;
+          }
+          if (bad && p.err) record_error(p.err, 1, t, c);
         }
-        if (bad && p.err) record_error(p.err, 1, t, c);
       }
     }
+    p.out[(int64_t)t * p.out_stride + c] = v;
   }
-  p.out[(int64_t)t * p.out_stride + c] = v;
 }
 
 __global__ void clear_error_kernel(int32_t* err) {
@@ -1570,7 +1587,7 @@ hipError_t launch_clear_error(int32_t* err, hipStream_t stream) {
 }
 
 hipError_t launch_build_indices(const BuildParams& p, hipStream_t stream) {
-  const int64_t blocks = (int64_t)p.T * ((p.W + p.K2 + 255) / 256);
+  const int64_t blocks = (int64_t)p.T * ((p.W + p.K2 + 256 * kBuildCols - 1) / (256 * kBuildCols));
   hipLaunchKernelGGL(build_indices_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
