@@ -137,3 +137,45 @@ def test_built_table_feeds_the_decode_like_the_page_table_form():
         comp_topk_lens=cl)
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
     assert np.array_equal(lens.cpu().numpy(), ref_lens)
+
+
+def test_graph_replays_of_the_builder_match_eager():
+    """The builder with an error block (cleared by a kernel, not a memset)
+    captured into a HIP graph and replayed four times, with eager work and
+    synchronisation in between, gives the eager result every time."""
+    need_gpu()
+    c = case(12, T=9, K2=700)
+    d = lambda a: torch.from_numpy(a).cuda()
+    T, K = c["swa"].shape[0], c["swa"].shape[1] + c["comp"].shape[1]
+    args = [d(c["swa"]), d(c["comp"]), d(c["cl"]), d(c["bt"]), d(c["tok2req"]), d(c["vt"])]
+    out = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    lens = torch.empty((T,), dtype=torch.int32, device="cuda")
+    err = torch.empty((4,), dtype=torch.int32, device="cuda")
+
+    def call():
+        L.build_indices(args[0], args[1], comp_local=True, comp_topk_lens=args[2],
+                        block_tables=args[3], page_size=c["ps"], token_to_req=args[4],
+                        valid_tokens=args[5], out=out, out_topk_lens=lens, err=err)
+    log("[builder] graph replays T=9")
+    call()
+    torch.cuda.synchronize()
+    ref = (out.clone(), lens.clone(), err.clone())
+    assert int(ref[2][0].item()) == 1          # the case has untranslatable entries
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):              # warm-up off the capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        out.fill_(7)                           # eager work between replays
+        lens.fill_(7)
+        err.fill_(7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lens, ref[1]), rep
+        assert int(err[0].item()) == 1, rep
