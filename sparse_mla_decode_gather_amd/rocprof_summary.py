@@ -5,7 +5,8 @@
         <fetch_dir> <write_dir> <copy_bytes> <cmd>
     python -m sparse_mla_decode_gather_amd.rocprof_summary sq <cmd> <dir>...
 
-``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv).
+``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv): the
+decode, combine and combined-table builder kernels.
 ``sq`` gives the median per dispatch of every counter in one or more
 --pmc runs over the decode kernels, with the MFMA-busy and waiting
 fractions derived from them.
@@ -53,7 +54,8 @@ def stats(directory: str, cmd: str) -> str:
              "kernel | calls | average_ns | min_ns | max_ns | percent"]
     for r in rows:
         name = r["Name"]
-        if any(d in name for d in DECODE) or "combine_kernel" in name:
+        if any(d in name for d in DECODE) or "combine_kernel" in name or \
+                "build_indices_kernel" in name:
             short = name.replace("smla::(anonymous namespace)::", "")
             short = short.replace("void ", "").split("(smla::")[0]
             lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
