@@ -357,8 +357,6 @@ def test_streaming_row_loads_match_plain_loads():
         axis=1)
     lens = g.integers(1, K + 1, size=T)
     w = custom(idx, lens, swa_rows=600, comp_rows=4000, seed=21)
-    log(f"[parity] streaming vs plain loads: T={T} K={K} and T=8")
-    big, lbig = run_decode(w, plan=L.plan_splits(T, 128, K, num_splits=1))
     n = 8
     small = W.Workload(
         name="custom8", T=n, H=w.H, K=K, q=w.q[:n].contiguous(), q_dtype=w.q_dtype,
@@ -366,9 +364,12 @@ def test_streaming_row_loads_match_plain_loads():
         indices=w.indices[:n].contiguous(), topk_lens=w.topk_lens[:n].contiguous(),
         seq_lens=w.seq_lens[:n].contiguous(), cum_seq_lens_q=None, sinks=w.sinks,
         bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, lse_scale=w.lse_scale)
-    out, lse = run_decode(small, plan=L.plan_splits(n, 128, K, num_splits=1))
-    assert torch.equal(out.view(torch.int16), big[:n].view(torch.int16))
-    assert torch.equal(lse, lbig[:n])
+    for S in (1, 4):
+        log(f"[parity] streaming vs plain loads: T={T} K={K} and T=8, {S} split(s)")
+        big, lbig = run_decode(w, plan=L.plan_splits(T, 128, K, num_splits=S))
+        out, lse = run_decode(small, plan=L.plan_splits(n, 128, K, num_splits=S))
+        assert torch.equal(out.view(torch.int16), big[:n].view(torch.int16)), S
+        assert torch.equal(lse, lbig[:n]), S
     check(w, tokens=range(0, T, 16), plan=L.plan_splits(T, 128, K, num_splits=1),
           what="streaming loads vs oracle")
 
