@@ -26,7 +26,8 @@ T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
 back-to-back launches.
 
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
---no-cpu-baseline, --sweep.
+--no-cpu-baseline, --sweep, --all-workloads (adds the other configurations:
+tiny, batched with sinks, FP8, speculative decode).
 """
 
 import argparse
@@ -188,6 +189,52 @@ def cpu_baseline(w, budget_s=10.0):
                       f"workload (NumPy float64 oracle, {secs:.1f} s)"}
 
 
+MFMA_PEAK_BY_ROWS = {"bf16": MFMA_BF16_PEAK_TFLOPS, "fp8_e4m3fn": MFMA_BF16_PEAK_TFLOPS}
+
+
+def other_workloads(stream):
+    """The other configurations with their default plans: per-launch time
+    (HIP events around 30 back-to-back launches, and HIP-graph replays),
+    gathered bytes and FLOPs of the active slots, and the fraction of the
+    roofline max(bytes / HBM peak, FLOPs / MFMA peak).  FP8 rows are widened
+    to BF16 and multiplied on BF16 MFMA, so BF16 is the MFMA peak."""
+    import torch
+    from sparse_mla_decode_gather_amd import lib, workloads as W
+    res = {}
+    for name, make in (("tiny", W.make_tiny), ("batched_sinks", W.make_batched_sinks),
+                       ("fp8", W.make_fp8), ("spec_decode", W.make_spec_decode)):
+        w = make("cuda")
+        n = active_slots_per_token(w)
+        rb = 1024 if w.kv_dtype == W.BF16 else 512
+        gathered = int(n.sum()) * rb
+        flops = 4.0 * 512 * w.H * int(n.sum())
+        out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+        plan = lib.plan_splits(w.T, w.H, w.K, lib.dtype_code(w.q),
+                               lib.dtype_code(w.swa_pool))
+        ws = lib.alloc_workspace(plan, w.T, w.H)
+
+        def st(w=w, out=out, lse=lse, plan=plan, ws=ws):
+            lib.decode_workload(w, out, lse, plan=plan, workspace=ws)
+        _, per = time_launches(st, 30, 5, stream)
+        avg = sum(per) / len(per)
+        gms = time_graph(st)
+        t_roof = max(gathered / (HBM_PEAK_GBPS * 1e9),
+                     flops / (MFMA_PEAK_BY_ROWS[w.kv_dtype] * 1e12))
+        res[name] = {"T": w.T, "H": w.H, "K": w.K, "q": w.q_dtype, "kv": w.kv_dtype,
+                     "num_splits": plan.num_splits, "gathered_bytes": gathered,
+                     "launch_us": round(avg * 1e3, 2),
+                     "graph_launch_us": round(gms * 1e3, 2),
+                     "gathered_GBps": round(gathered / (gms * 1e-3) / 1e9, 1),
+                     "tflops": round(flops / (gms * 1e-3) / 1e12, 1),
+                     "bound": "hbm" if gathered / (HBM_PEAK_GBPS * 1e9) >=
+                              flops / (MFMA_PEAK_BY_ROWS[w.kv_dtype] * 1e12) else "mfma",
+                     "roofline_frac": round(t_roof / (gms * 1e-3), 4)}
+        del w, out, lse, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,6 +243,10 @@ def main():
     ap.add_argument("--T", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="also time the other configurations (tiny, batched "
+                         "with sinks, FP8, speculative decode) with their "
+                         "default plans")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy three "
                          "times (known bytes) for counter calibration")
@@ -377,6 +428,8 @@ def main():
                 sweep[str(t)]["graph_launch_us"] = round(gms * 1e3, 2)
                 sweep[str(t)]["graph_gathered_GBps"] = round(g / (gms * 1e-3) / 1e9, 1)
         result["sweep"] = sweep
+    if args.all_workloads:
+        result["workloads"] = other_workloads(stream)
     if args.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1)
         dst = torch.empty_like(src)
