@@ -817,11 +817,46 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   const int l32 = lane & 31;
   const int kg = lane >> 5;
 
-  // XCD-aware work mapping (see decode_kernel).
+  // XCD-aware work mapping (see decode_kernel): XCD x owns the contiguous
+  // item range [lo, lo + cnt) and starts its workgroups in the order of
+  // blockIdx.x >> 3.  With per-token lengths, the items of the range are
+  // started longest first (rank by active columns of the item's split, ties
+  // by position): with one or two items per CU, taking them in token order
+  // lets the CUs that draw two long tokens set the end of a ragged batch
+  // (~9% at 512 tokens of topk_len uniform in [1024, 2048]); longest-first
+  // recovers it for ~0.5% on uniform batches.  The ranking uses slots[],
+  // which the compaction fills only later.  Combined table form, up to one
+  // item per thread.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int q8 = nblk >> 3, r8 = nblk & 7;
-  const int item = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
+  const int lo = xcd * q8 + min(xcd, r8);
+  int item = lo + (blockIdx.x >> 3);
+  if constexpr (!GEN) {
+    const int cnt = q8 + (xcd < r8 ? 1 : 0);
+    if (p.topk_lens != nullptr && cnt > 1 && cnt <= NT) {
+      const int tid = threadIdx.x;
+      int my_len = -1;
+      if (tid < cnt) {
+        const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
+        const int L = min(max(p.topk_lens[ti], 0), p.K);
+        my_len = min(max(L - si * p.split_cols, 0), p.split_cols);
+        slots[tid] = my_len;
+      }
+      __syncthreads();
+      if (tid < cnt) {
+        int rank = 0;
+        for (int k = 0; k < cnt; ++k) {
+          const int lk = slots[k];
+          rank += (lk > my_len || (lk == my_len && k < tid)) ? 1 : 0;
+        }
+        if (rank == (int)(blockIdx.x >> 3)) slots[kSegHd] = lo + tid;
+      }
+      __syncthreads();
+      item = slots[kSegHd];
+      __syncthreads();   // slots[] is rewritten by the compaction
+    }
+  }
   const int t = item / p.S;
   const int s = item - t * p.S;
   const int head = wave * 32 + l32;       // head of this lane's S^T column

@@ -374,6 +374,36 @@ def test_streaming_row_loads_match_plain_loads():
           what="streaming loads vs oracle")
 
 
+def test_ragged_batch_order_does_not_change_any_token():
+    """Workgroups start the items of their XCD longest first, so permuting
+    the tokens of a ragged batch reassigns every item to another workgroup;
+    each token's output and LSE must stay bit-identical (unsplit and split),
+    and match the oracle on samples."""
+    need_gpu()
+    T, K = 256, 2048
+    g = np.random.default_rng(31)
+    idx = np.concatenate([
+        np.stack([g.choice(600, 128, replace=False) for _ in range(T)]),
+        np.stack([g.choice(4000, K - 128, replace=False) for _ in range(T)])], axis=1)
+    lens = g.integers(1, K + 1, size=T)
+    w = custom(idx, lens, swa_rows=600, comp_rows=4000, seed=23)
+    perm = torch.as_tensor(g.permutation(T)).cuda()
+    wp = W.Workload(
+        name="permuted", T=T, H=w.H, K=K, q=w.q[perm].contiguous(), q_dtype=w.q_dtype,
+        swa_pool=w.swa_pool, comp_pool=w.comp_pool, kv_dtype=w.kv_dtype,
+        indices=w.indices[perm].contiguous(), topk_lens=w.topk_lens[perm].contiguous(),
+        seq_lens=w.seq_lens[perm].contiguous(), cum_seq_lens_q=None, sinks=w.sinks,
+        bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, lse_scale=w.lse_scale)
+    for S in (1, 3):
+        log(f"[parity] ragged batch T={T} permuted, {S} split(s)")
+        plan = L.plan_splits(T, 128, K, num_splits=S)
+        a, la = run_decode(w, plan=plan)
+        b, lb = run_decode(wp, plan=plan)
+        assert torch.equal(a[perm].view(torch.int16), b.view(torch.int16)), S
+        assert torch.equal(la[perm], lb), S
+    check(w, tokens=range(0, T, 32), what="ragged batch vs oracle")
+
+
 def test_indices_past_topk_len_are_never_read():
     """Columns at or beyond topk_len hold indices far outside both pools;
     they must not be dereferenced (the result equals the table with those
