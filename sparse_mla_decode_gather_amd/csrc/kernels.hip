@@ -825,22 +825,31 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   // lets the CUs that draw two long tokens set the end of a ragged batch
   // (~9% at 512 tokens of topk_len uniform in [1024, 2048]); longest-first
   // recovers it for ~0.5% on uniform batches.  The ranking uses slots[],
-  // which the compaction fills only later.  Combined table form, up to one
-  // item per thread.
+  // which the compaction fills only later.  Up to one item per thread.
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
   const int q8 = nblk >> 3, r8 = nblk & 7;
   const int lo = xcd * q8 + min(xcd, r8);
   int item = lo + (blockIdx.x >> 3);
-  if constexpr (!GEN) {
+  {
     const int cnt = q8 + (xcd < r8 ? 1 : 0);
-    if (p.topk_lens != nullptr && cnt > 1 && cnt <= NT) {
+    const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
+                            : p.topk_lens != nullptr;
+    if (ragged && cnt > 1 && cnt <= NT) {
       const int tid = threadIdx.x;
       int my_len = -1;
       if (tid < cnt) {
+        // active columns of the item's split: [0, L1) and, for the general
+        // table view, [P, P + L2), intersected with the split's columns
         const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
-        const int L = min(max(p.topk_lens[ti], 0), p.K);
-        my_len = min(max(L - si * p.split_cols, 0), p.split_cols);
+        int a, b;
+        token_length_loads<GEN>(p, ti, a, b);
+        TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
+        token_lengths<GEN>(p, a, b, ti_tab);
+        const int c0 = si * p.split_cols, c1 = c0 + p.split_cols;
+        my_len = max(0, min(ti_tab.L1, c1) - c0);
+        if constexpr (GEN)
+          my_len += max(0, min(ti_tab.P + ti_tab.L2, c1) - max(ti_tab.P, c0));
         slots[tid] = my_len;
       }
       __syncthreads();
