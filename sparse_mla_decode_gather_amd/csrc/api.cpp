@@ -388,7 +388,8 @@ int sparse_mla_build_indices(const smla_build_args* a, smla_stream_t stream_hand
       (!a->block_tables || a->max_blocks < 1 || a->page_size < 1 ||
        a->num_requests < 1 || sb < a->max_blocks))
     return SMLA_ERR_INVALID_ARG;
-  if ((int64_t)a->T * ((K + 255) / 256) > INT_MAX) return SMLA_ERR_INVALID_ARG;
+  // one workgroup per 1024 columns of a token (the builder kernel's tile)
+  if ((int64_t)a->T * ((K + 1023) / 1024) > INT_MAX) return SMLA_ERR_INVALID_ARG;
   const void* ptrs[] = {a->swa_indices, a->comp_indices, a->comp_topk_lens,
                         a->block_tables, a->token_to_req, a->valid_tokens,
                         a->out_indices, a->out_topk_lens, a->err};
