@@ -374,13 +374,14 @@ def test_streaming_row_loads_match_plain_loads():
           what="streaming loads vs oracle")
 
 
-def test_ragged_batch_order_does_not_change_any_token():
+@pytest.mark.parametrize("T", [256, 250])     # 250: XCD ranges of unequal size
+def test_ragged_batch_order_does_not_change_any_token(T):
     """Workgroups start the items of their XCD longest first, so permuting
     the tokens of a ragged batch reassigns every item to another workgroup;
     each token's output and LSE must stay bit-identical (unsplit and split),
     and match the oracle on samples."""
     need_gpu()
-    T, K = 256, 2048
+    K = 2048
     g = np.random.default_rng(31)
     idx = np.concatenate([
         np.stack([g.choice(600, 128, replace=False) for _ in range(T)]),
