@@ -57,11 +57,6 @@ constexpr int kRowBytes = kD * 2;  // a BF16 row
 // a per-lane base plus a compile-time immediate.
 constexpr int kRowPitch = kRowBytes + 48;
 constexpr int kTileBytes = kTile * kRowPitch;
-// LDS row pitch of an FP8 row kept as FP8 (H=64 with FP8 q and rows): 512
-// bytes plus 16 (pitch = 4 dwords mod 64 banks), so the 32-byte S^T operand
-// reads of 16 consecutive rows and the 8-bit transposing reads of the V^T
-// operands (4 rows x 2 eight-byte words per 16 lanes) hit distinct banks.
-constexpr int kRowPitch8 = kD + 16;
 constexpr float kLog2e = 1.4426950408889634f;
 // A tile may exceed the running reference max by this much (base-2 logit
 // units) before the split is restarted with a higher reference: with
@@ -75,8 +70,6 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // element conversions
@@ -157,26 +150,6 @@ __device__ __forceinline__ void mfma_qk(f32x16& acc, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void mfma_qk_drain(f32x16& acc) {
   asm("s_nop 7\n\ts_nop 7\n\ts_nop 1" : "+v"(acc));
-}
-
-// S^T from FP8 q and FP8 rows on the gfx950 FP8 MFMA (32x32x64, 16 passes,
-// E4M3 x E4M3 products are exact, fp32 accumulation): lane l supplies 32
-// bytes of row l%32 (A) and of head l%32 (B) for the same 32 dims, and the
-// accumulator has the layout of the BF16 32x32 MFMA (both measured on the
-// GPU).  Same conventions as the BF16 asm above: VGPR accumulator, 2 wait
-// states before each MFMA for VALU-written operands, and 24 (more than the
-// 20 the compiler inserts) before a VALU read of the result.
-__device__ __forceinline__ f32x16 mfma_qk8_first(i32x8 a, i32x8 b) {
-  f32x16 d;
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, 0"
-      : "=&v"(d) : "v"(a), "v"(b));
-  return d;
-}
-__device__ __forceinline__ void mfma_qk8(f32x16& acc, i32x8 a, i32x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_qk8_drain(f32x16& acc) {
-  asm("s_nop 15\n\ts_nop 7" : "+v"(acc));
 }
 
 template <int N>
@@ -384,12 +357,7 @@ void decode_kernel(DecodeParams p) {
   // loads for tile it+NSTAGE-1 are in flight while tile it is computed.
   constexpr bool USE_DMA = !KV_FP8;
   constexpr int NSTAGE = KV_FP8 ? 2 : (NW == 4 ? 4 : 2);
-  // FP8 q and FP8 rows: the rows stay FP8 in LDS, S^T runs on the FP8 MFMA
-  // and the V^T operands are widened to BF16 as they are read.
-  constexpr bool F8 = Q_FP8 && KV_FP8;
-  constexpr int kPitch = F8 ? kRowPitch8 : kRowPitch;
-  constexpr int kTileB = kTile * kPitch;
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileB];
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t slots[kSeg];
   __shared__ int32_t wave_cnt[NW];
   __shared__ int32_t restart_flag;
@@ -428,31 +396,19 @@ void decode_kernel(DecodeParams p) {
   const int c_end = min(tt.end(), c_begin + p.split_cols);
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds head `head`,
-  // dims [16kk + 8kg, +8) for each 16-dim step kk; with FP8 rows and q
-  // (F8), the raw bytes of dims [64kk + 32kg, +32) for each 64-dim step.
-  bf16x8 qf[F8 ? 1 : 32];
-  i32x8 qf8[F8 ? 8 : 1];
+  // dims [16kk + 8kg, +8) for each 16-dim step kk.
+  bf16x8 qf[32];
   {
     const size_t qrow = ((size_t)t * H + head) * kD;
-    if constexpr (F8) {
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const uint8_t* src = (const uint8_t*)p.q + qrow + kk * 64 + kg * 32;
-        const u32x4 lo = *(const u32x4*)src;
-        const u32x4 hi = *(const u32x4*)(src + 16);
-        qf8[kk] = __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
-        const int d0 = kk * 16 + kg * 8;
-        u32x4 v;
-        if constexpr (Q_FP8)
-          v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
-        else
-          v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
-        qf[kk] = __builtin_bit_cast(bf16x8, v);
-      }
+    for (int kk = 0; kk < 32; ++kk) {
+      const int d0 = kk * 16 + kg * 8;
+      u32x4 v;
+      if constexpr (Q_FP8)
+        v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
+      else
+        v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
   // Drain the Q loads here: otherwise their waits land inside the tile
@@ -486,59 +442,25 @@ void decode_kernel(DecodeParams p) {
   // pinned with scheduling barriers (the compiler then counts the LDS reads
   // in flight and waits for exactly the one each MFMA needs).
   constexpr int kLead = 4;
-  // F8: lane l reads 32 bytes of row l%32 (dims [64kk + 32kg, +32)), and
-  // the V^T operand of rows 16h.. / dims 32db.. through 8-bit transposing
-  // reads: input lane i of each 16-lane group G points at row
-  // 8(i/8) + 4(G/2) + (i/2)%4 and dims 16(G%2) + 8(i%2) of the block, so that
-  // output element e of lane l is row 8(e/4) + 4(l/32) + e%4 (the P^T k-slot
-  // order, see tile_row_of_reg) of dim l%32.
-  const int qk8_off = l32 * kRowPitch8 + kg * 32;
-  const int tr8_off = (8 * ((lane & 15) >> 3) + 4 * (lane >> 5) + ((lane >> 1) & 3)) * kRowPitch8 +
-                      16 * ((lane >> 4) & 1) + 8 * (lane & 1);
   auto qk = [&](const uint8_t* tb, auto&& every4) -> f32x16 {
-    if constexpr (F8) {
-      auto rd = [&](int kk) -> i32x8 {
-        const uint8_t* a = tb + qk8_off + kk * 64;
-        const u32x4 lo = *(const u32x4*)a;
-        const u32x4 hi = *(const u32x4*)(a + 16);
-        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      i32x8 a8[2];
-      a8[0] = rd(0);
-      a8[1] = rd(1);
-      f32x16 acc;
+    bf16x8 a[kLead];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk == 0) acc = mfma_qk8_first(a8[0], qf8[0]);
-        else mfma_qk8(acc, a8[kk & 1], qf8[kk]);
-        if (kk + 2 < 8) a8[kk & 1] = rd(kk + 2);
-        __builtin_amdgcn_sched_barrier(0);
-        every4(kk);
-      }
+    for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
+    f32x16 acc;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
-      mfma_qk8_drain(acc);
-      return acc;
-    } else {
-      bf16x8 a[kLead];
-#pragma unroll
-      for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
-      f32x16 acc;
-#pragma unroll
-      for (int kk = 0; kk < 32; ++kk) {
+      if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
+      else mfma_qk(acc, a[kk % kLead], qf[kk]);
+      if (kk + kLead < 32)
+        a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
+      if ((kk & 3) == 3) {
         __builtin_amdgcn_sched_barrier(0);
-        if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
-        else mfma_qk(acc, a[kk % kLead], qf[kk]);
-        if (kk + kLead < 32)
-          a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
-        if ((kk & 3) == 3) {
-          __builtin_amdgcn_sched_barrier(0);
-          every4(kk >> 2);
-        }
+        every4(kk >> 2);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      return acc;
     }
+    __builtin_amdgcn_sched_barrier(0);
+    return acc;
   };
 
   // Online softmax of one tile's S^T; returns P^T as the two B operands of
@@ -581,52 +503,26 @@ void decode_kernel(DecodeParams p) {
   // O^T += V^T P^T for a tile: step k covers rows [16h, 16h+16) (h = k/16)
   // of d-block db = k%16.
   auto pv = [&](const uint8_t* tb, const bf16x8 (&pf)[2]) {
-    if constexpr (F8) {
-      // The 8-bit reads run kLead8 steps ahead and each is widened one
-      // step before its MFMA, so the widening never waits on LDS latency.
-      constexpr int kLead8 = 6;
-      auto rd8 = [&](int k) -> u32x2 {
-        const uint8_t* vb = tb + tr8_off + (16 * (k >> 4)) * kRowPitch8 + (k & 15) * 32;
-        return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (i32x2 __attribute__((address_space(3)))*)(vb)));
-      };
-      u32x2 raw[kLead8];
+    auto vfrag = [&](int k) -> bf16x8 {
+      const uint8_t* vb = tb + tr_off + (16 * (k >> 4)) * kRowPitch + (k & 15) * 64;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+      return __builtin_bit_cast(bf16x8,
+                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 v[kLead];
 #pragma unroll
-      for (int k = 0; k < kLead8; ++k) raw[k] = rd8(k);
-      bf16x8 v[2];
-      v[0] = __builtin_bit_cast(bf16x8, widen_e4m3fn_x8(raw[0]));
+    for (int k = 0; k < kLead; ++k) v[k] = vfrag(k);
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k & 1], pf[k >> 4],
-                                                           o[k & 15], 0, 0, 0);
-        if (k + kLead8 < 32) raw[k % kLead8] = rd8(k + kLead8);
-        if (k + 1 < 32)
-          v[(k + 1) & 1] = __builtin_bit_cast(bf16x8, widen_e4m3fn_x8(raw[(k + 1) % kLead8]));
-      }
+    for (int k = 0; k < 32; ++k) {
       __builtin_amdgcn_sched_barrier(0);
-    } else {
-      auto vfrag = [&](int k) -> bf16x8 {
-        const uint8_t* vb = tb + tr_off + (16 * (k >> 4)) * kRowPitch + (k & 15) * 64;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(vb));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
-        return __builtin_bit_cast(bf16x8,
-                                  __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      };
-      bf16x8 v[kLead];
-#pragma unroll
-      for (int k = 0; k < kLead; ++k) v[k] = vfrag(k);
-#pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        __builtin_amdgcn_sched_barrier(0);
-        o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k % kLead], pf[k >> 4],
-                                                           o[k & 15], 0, 0, 0);
-        if (k + kLead < 32) v[k % kLead] = vfrag(k + kLead);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k % kLead], pf[k >> 4],
+                                                         o[k & 15], 0, 0, 0);
+      if (k + kLead < 32) v[k % kLead] = vfrag(k + kLead);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   bool again;
@@ -677,7 +573,7 @@ void decode_kernel(DecodeParams p) {
     // repeats the last active row.  Slot codes are wave-uniform: they are
     // read into SGPRs and row addresses are computed on the scalar unit.
     auto stage = [&](int tile) -> const uint8_t* {
-      return kv_lds + (tile % NSTAGE) * kTileB;
+      return kv_lds + (tile % NSTAGE) * kTileBytes;
     };
 
     if constexpr (USE_DMA) {
@@ -771,18 +667,13 @@ void decode_kernel(DecodeParams p) {
         st[jj] = *(const stage_t*)(row + lane_off);
       };
       auto store = [&](int tile) {
-        uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileB;
+        uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
 #pragma unroll
         for (int jj = 0; jj < RPW; ++jj) {
-          if constexpr (F8) {
-            // the row stays FP8: lane i's 8 bytes at byte 8i of the row
-            *(u32x2*)(dst + (wave_u * RPW + jj) * kRowPitch8 + lane * 8) = st[jj];
-          } else {
-            u32x4 v;
-            if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
-            else v = st[jj];
-            *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
-          }
+          u32x4 v;
+          if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
+          else v = st[jj];
+          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
         }
       };
       // prologue: tiles 0 .. NSTAGE-2 into their stages

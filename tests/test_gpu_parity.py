@@ -121,12 +121,17 @@ def test_full_size_long_context_batch_sampled():
 # selection and masking, bit-exact
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("H", [64, 128])
-def test_selection_probe_exact(H):
+@pytest.mark.parametrize("H,dt", [(64, W.BF16), (128, W.BF16), (64, W.FP8),
+                                   (128, W.FP8)])
+def test_selection_probe_exact(H, dt):
     """q = 0 and no sink, pool row r = one-hot e_{r mod 512}: every logit is
     0, so 2^lse is the active-slot count and count*out[d] is the number of
-    active slots whose row is d mod 512 -- exact integers on both sides."""
+    active slots whose row is d mod 512 -- exact integers on both sides.
+    E4M3 holds 0 and 1 exactly, so the FP8 form (FP8 q and rows: the FP8
+    MFMA and the 8-bit transposing V^T reads at H=64) is exact too."""
     need_gpu()
+    code = L.DTYPE_FP8_E4M3FN if dt == W.FP8 else L.DTYPE_BF16
+    tdt = torch.float8_e4m3fn if dt == W.FP8 else torch.bfloat16
     rng = np.random.default_rng(5)
     T, K = 9, 600
     idx = np.empty((T, K), np.int32)
@@ -141,16 +146,17 @@ def test_selection_probe_exact(H):
     comp = torch.zeros((1500, 512), dtype=torch.bfloat16)
     comp[torch.arange(1500), torch.arange(1500) % 512] = 1
     w = W.Workload(name="probe", T=T, H=H, K=K,
-                   q=torch.zeros((T, H, 512), dtype=torch.bfloat16, device="cuda"),
-                   q_dtype=W.BF16, swa_pool=swa.cuda(), comp_pool=comp.cuda(),
-                   kv_dtype=W.BF16, indices=torch.from_numpy(idx).cuda(),
+                   q=torch.zeros((T, H, 512), dtype=torch.bfloat16,
+                                 device="cuda").to(tdt),
+                   q_dtype=dt, swa_pool=swa.to(tdt).cuda(), comp_pool=comp.to(tdt).cuda(),
+                   kv_dtype=dt, indices=torch.from_numpy(idx).cuda(),
                    topk_lens=torch.from_numpy(lens).cuda(),
                    seq_lens=torch.full((T,), 9000, dtype=torch.int32,
                                        device="cuda"),
                    cum_seq_lens_q=None, sinks=None, bmm1_scale=0.3,
                    bmm2_scale=1.0)
     for S in (1, 3):
-        out, lse = run_decode(w, plan=L.plan_splits(T, H, K, num_splits=S))
+        out, lse = run_decode(w, plan=L.plan_splits(T, H, K, code, code, num_splits=S))
         o, l = out.float().cpu().numpy(), lse.cpu().numpy()
         for t in range(T):
             slots = oracle.active_slots(idx[t], lens[t])
@@ -209,24 +215,28 @@ def test_large_logit_range_restarts_are_exact():
     check(w, what="wide logits S=4", plan=L.plan_splits(4, 128, 1528, num_splits=4))
 
 
-def test_increasing_logits_force_repeated_restarts():
+@pytest.mark.parametrize("dt", [W.BF16, W.FP8])
+def test_increasing_logits_force_repeated_restarts(dt):
     """Row i of the table is (i/40)*u for a fixed direction u and q = u, so
-    the logits rise by ~100 (base-2) every 32-row tile."""
+    the logits rise by ~37 (base-2) every 32-row tile and the 64 units of
+    slack are outgrown every other tile.  FP8 rows round i/40 to E4M3 (the
+    oracle reads the same bits) and run on the FP8 MFMA at H=64."""
     need_gpu()
     T, K, H = 2, 700, 64
+    tdt = torch.float8_e4m3fn if dt == W.FP8 else torch.bfloat16
     u = torch.zeros(512)
     u[:8] = 1.0
-    rows = torch.stack([u * (i / 40.0) for i in range(K)]).to(torch.bfloat16)
+    rows = torch.stack([u * (i / 40.0) for i in range(K)]).to(tdt)
     idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
     idx[:, :128] = np.arange(128)
     w = W.Workload(name="rising", T=T, H=H, K=K,
-                   q=u.to(torch.bfloat16).expand(T, H, 512).contiguous().cuda(),
-                   q_dtype=W.BF16, swa_pool=rows.cuda(), comp_pool=rows.cuda(),
-                   kv_dtype=W.BF16, indices=torch.from_numpy(idx).cuda(),
+                   q=u.to(tdt).expand(T, H, 512).contiguous().cuda(),
+                   q_dtype=dt, swa_pool=rows.cuda(), comp_pool=rows.cuda(),
+                   kv_dtype=dt, indices=torch.from_numpy(idx).cuda(),
                    topk_lens=None,
                    seq_lens=torch.full((T,), 4096, dtype=torch.int32, device="cuda"),
                    cum_seq_lens_q=None, sinks=None, bmm1_scale=4.0, bmm2_scale=1.0)
-    check(w, what="rising logits")
+    check(w, what=f"rising logits {dt}")
 
 
 def test_duplicate_indices_count_per_slot():
@@ -250,12 +260,15 @@ def test_wide_table_multiple_segments():
     check(w, what="K=5000 S=3", plan=L.plan_splits(T, 128, K, num_splits=3))
 
 
-@pytest.mark.parametrize("q", [W.BF16, W.FP8])
-def test_fp8_rows_at_h128_edges_segments_and_restarts(q):
+@pytest.mark.parametrize("H,q", [(128, W.BF16), (128, W.FP8), (64, W.BF16),
+                                  (64, W.FP8)])
+def test_fp8_rows_edges_segments_and_restarts(H, q):
     """FP8 rows at H=128 take the register-staged path of the H=128 kernel
     (two register sets, an extra all-masked tile when the tile count is
-    odd).  Ragged and tiny lengths give odd, single and empty tile counts;
-    K=5000 crosses segments; wide logits force restarts."""
+    odd); at H=64 with FP8 q the rows stay FP8 in LDS and S^T runs on the
+    FP8 MFMA, with BF16 q they are widened at the store.  Ragged and tiny
+    lengths give odd, single and empty tile counts; K=5000 crosses
+    segments; wide logits force restarts."""
     need_gpu()
     qc = L.DTYPE_FP8_E4M3FN if q == W.FP8 else L.DTYPE_BF16
     kc = L.DTYPE_FP8_E4M3FN
@@ -267,18 +280,18 @@ def test_fp8_rows_at_h128_edges_segments_and_restarts(q):
     idx[5, ::3] = -1
     idx[6, 200:230] = idx[6, 300]          # duplicates count per slot
     lens = [0, 1, 31, 32, 33, 127, 128, 129, 700, 650, 64, 97]
-    w = custom(idx, lens=lens, H=128, kv=W.FP8, q=q)
-    check(w, what=f"fp8 rows H=128 q={q} edges")
-    check(w, plan=L.plan_splits(T, 128, K, qc, kc, num_splits=5),
-          what=f"fp8 rows H=128 q={q} edges S=5")
+    w = custom(idx, lens=lens, H=H, kv=W.FP8, q=q)
+    check(w, what=f"fp8 rows H={H} q={q} edges")
+    check(w, plan=L.plan_splits(T, H, K, qc, kc, num_splits=5),
+          what=f"fp8 rows H={H} q={q} edges S=5")
 
     T, K = 3, 5000
     idx = np.concatenate([rng.integers(0, 600, (T, 128)),
                           rng.integers(0, 20000, (T, K - 128))], 1).astype(np.int32)
     idx[1, 4000:] = -1
-    w = custom(idx, lens=[5000, 4500, 2100], comp_rows=20000, H=128, kv=W.FP8, q=q)
-    check(w, what=f"fp8 rows H=128 q={q} K=5000",
-          plan=L.plan_splits(T, 128, K, qc, kc, num_splits=1))
+    w = custom(idx, lens=[5000, 4500, 2100], comp_rows=20000, H=H, kv=W.FP8, q=q)
+    check(w, what=f"fp8 rows H={H} q={q} K=5000",
+          plan=L.plan_splits(T, H, K, qc, kc, num_splits=1))
 
     idx = np.concatenate([rng.integers(0, 600, (4, 128)),
                           rng.integers(0, 900, (4, 1400))], 1).astype(np.int32)
@@ -286,10 +299,10 @@ def test_fp8_rows_at_h128_edges_segments_and_restarts(q):
     # fold it) and the logit spread - hence the restarts - matches the BF16
     # case; unscaled, the LSE would sit near 5e4, where one fp32 ulp already
     # exceeds the 1e-3 LSE bar.
-    w = custom(idx, lens=[1528, 900, 200, 1528], H=128, kv=W.FP8, q=q,
+    w = custom(idx, lens=[1528, 900, 200, 1528], H=H, kv=W.FP8, q=q,
                b1=2.0 * (0.05 if q == W.FP8 else 1.0))
-    check(w, what=f"fp8 rows H=128 q={q} wide logits",
-          plan=L.plan_splits(4, 128, 1528, qc, kc, num_splits=1))
+    check(w, what=f"fp8 rows H={H} q={q} wide logits",
+          plan=L.plan_splits(4, H, 1528, qc, kc, num_splits=1))
 
 
 def test_padded_pool_rows():
