@@ -205,14 +205,24 @@ __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
   }
 }
 
-// 8 bytes of a row through a global (not flat) pointer: row addresses are
-// rebuilt from integers, and flat loads also count in lgkmcnt, which would
-// make every LDS wait of the tile loop wait for HBM too.
+// 8 bytes through a global (not flat) pointer (FP8 q: a per-lane head
+// row): flat loads also count in lgkmcnt, which would make LDS waits wait
+// for HBM too.
 typedef u32x2 __attribute__((address_space(1))) global_u32x2;
 __device__ __forceinline__ u32x2 load_global8(const uint8_t* row, uint32_t off) {
   return *(const global_u32x2*)(row + off);
 }
 typedef u32x4 __attribute__((address_space(1))) global_u32x4;
+// 8 bytes per lane of a 512-byte FP8 row from a uniform row address: a
+// buffer load with the row as a scalar resource and a 32-bit lane offset.
+// The global form needs a 64-bit address per lane, built by the VALU for
+// every row; this form measured 1.5-2.5% faster on FP8-row decodes, with
+// the same bytes.  The resource covers exactly the row (offsets past it
+// would read 0).
+__device__ __forceinline__ u32x2 load_row8(const uint8_t* row, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, 512, 0x00020000);
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0));
+}
 typedef int32_t __attribute__((address_space(1))) global_i32;
 
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
@@ -640,12 +650,13 @@ void decode_kernel(DecodeParams p) {
         pv(stage(it), pf);
       }
     } else {
-      // Register-staged gather: lane `lane` carries 16 B of a BF16 row (8 B
-      // of an FP8 row, widened to BF16 when written to LDS).  The loads of
-      // tile it+NSTAGE-1 are issued while the S^T MFMAs of tile it run and
-      // written to LDS after its O^T MFMAs, into the stage tile it-1 used.
-      constexpr int VW = KV_FP8 ? 2 : 4;          // dwords per lane per row
-      typedef uint32_t stage_t __attribute__((ext_vector_type(VW)));
+      // Register-staged gather of FP8 rows: lane `lane` carries 8 B of a row,
+      // widened to BF16 when written to LDS.  The loads of tile it+NSTAGE-1
+      // are issued while the S^T MFMAs of tile it run and written to LDS
+      // after its O^T MFMAs, into the stage tile it-1 used.
+      static_assert(KV_FP8, "register staging serves FP8 rows");
+      constexpr int VW = 2;                       // dwords per lane per row
+      typedef u32x2 stage_t;
       const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
       const uint32_t lane_off = (uint32_t)lane * (VW * 4);
       stage_t st[RPW];
@@ -664,7 +675,7 @@ void decode_kernel(DecodeParams p) {
         code = (s0 + jj < n_act) ? code : last_code;
         const uint8_t* base = code < 0 ? p.comp : p.swa;
         const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
-        st[jj] = *(const stage_t*)(row + lane_off);
+        st[jj] = load_row8(row, lane_off);
       };
       auto store = [&](int tile) {
         uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
@@ -1158,7 +1169,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         const uint32_t lane_off8 = (uint32_t)lane * 8u;
         auto load_set = [&](u32x2 (&rs)[RPW]) {
 #pragma unroll
-          for (int jj = 0; jj < RPW; ++jj) rs[jj] = load_global8(rows[jj], lane_off8);
+          for (int jj = 0; jj < RPW; ++jj) rs[jj] = load_row8(rows[jj], lane_off8);
         };
         auto store_set = [&](int tile, const u32x2 (&rs)[RPW]) {
           uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes + wave_u * RPW * kRowPitch +
@@ -1196,7 +1207,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           if constexpr (kQK) {
             sv = qk(stage(it), [&](int kk) {
               if (kLoad && (kk & 3) == 3)
-                rs_next[kk >> 2] = load_global8(rows[kk >> 2], lane_off8);
+                rs_next[kk >> 2] = load_row8(rows[kk >> 2], lane_off8);
             });
             mfma_qk_drain(sv);
             mask_tail(sv, it);
