@@ -305,15 +305,20 @@ def test_fp8_rows_edges_segments_and_restarts(H, q):
           plan=L.plan_splits(4, H, 1528, qc, kc, num_splits=1))
 
 
-def test_padded_pool_rows():
+@pytest.mark.parametrize("H", [64, 128])
+def test_padded_pool_rows(H):
+    """Pool rows with a larger stride than their 512 elements: every row
+    load (LDS-DMA, and for FP8 rows the per-row buffer resource) starts at
+    the row's own address."""
     need_gpu()
     rng = np.random.default_rng(4)
     idx = np.concatenate([rng.integers(0, 600, (4, 128)),
                           rng.integers(0, 900, (4, 200))], 1).astype(np.int32)
     for kv in (W.BF16, W.FP8):
-        w = custom(idx, kv=kv, row_stride=576)
-        assert w.swa_pool.stride(0) == 576
-        check(w, what=f"row stride 576 {kv}")
+        for q in ((W.BF16, W.FP8) if kv == W.FP8 else (W.BF16,)):
+            w = custom(idx, kv=kv, q=q, H=H, row_stride=576)
+            assert w.swa_pool.stride(0) == 576
+            check(w, what=f"row stride 576 H={H} kv={kv} q={q}")
 
 
 @pytest.mark.parametrize("q,kv,H", [(W.FP8, W.FP8, 128), (W.BF16, W.FP8, 64)])
