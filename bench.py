@@ -192,7 +192,10 @@ def cpu_baseline(w, budget_s=10.0):
 MFMA_PEAK_BY_ROWS = {"bf16": MFMA_BF16_PEAK_TFLOPS, "fp8_e4m3fn": MFMA_BF16_PEAK_TFLOPS}
 
 
-def other_workloads(stream):
+WORKLOAD_NAMES = ("tiny", "batched_sinks", "fp8", "spec_decode")
+
+
+def other_workloads(stream, only=None):
     """The other configurations with their default plans: per-launch time
     (HIP events around 30 back-to-back launches, and HIP-graph replays),
     gathered bytes and FLOPs of the active slots, and the fraction of the
@@ -203,6 +206,8 @@ def other_workloads(stream):
     res = {}
     for name, make in (("tiny", W.make_tiny), ("batched_sinks", W.make_batched_sinks),
                        ("fp8", W.make_fp8), ("spec_decode", W.make_spec_decode)):
+        if only is not None and name != only:
+            continue
         w = make("cuda")
         n = active_slots_per_token(w)
         rb = 1024 if w.kv_dtype == W.BF16 else 512
@@ -247,6 +252,10 @@ def main():
                     help="also time the other configurations (tiny, batched "
                          "with sinks, FP8, speculative decode) with their "
                          "default plans")
+    ap.add_argument("--only-workload", choices=WORKLOAD_NAMES,
+                    help="time only this other configuration (as --all-workloads "
+                         "does) and print its record instead of the headline "
+                         "line: a short command to run under a kernel tracer")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy three "
                          "times (known bytes) for counter calibration")
@@ -263,6 +272,10 @@ def main():
     lib.load()
     torch.cuda.set_device(0)
     stream = torch.cuda.current_stream()
+    if args.only_workload:
+        rec = other_workloads(stream, only=args.only_workload)[args.only_workload]
+        print(json.dumps({"workload": args.only_workload, **rec}), flush=True)
+        return
     w = W.make_long_context(args.T, "cuda", seed=4000 + args.T)
     n_act = active_slots_per_token(w)
     T = w.T
