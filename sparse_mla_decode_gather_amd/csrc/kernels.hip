@@ -219,8 +219,13 @@ typedef u32x4 __attribute__((address_space(1))) global_u32x4;
 // every row; this form measured 1.5-2.5% faster on FP8-row decodes, with
 // the same bytes.  The resource covers exactly the row (offsets past it
 // would read 0).
+// Word 3 of the buffer resource: DATA_FORMAT (bits 18:15) = 4, 32-bit
+// elements, which untyped loads need to be nonzero; no swizzle, no index
+// stride, default destination selects.
+constexpr int kRawBufferWord3 = 4 << 15;
 __device__ __forceinline__ u32x2 load_row8(const uint8_t* row, uint32_t off) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, 512, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, 512, kRawBufferWord3);
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, 0));
 }
 typedef int32_t __attribute__((address_space(1))) global_i32;
