@@ -306,6 +306,26 @@ def test_fp8_rows_edges_segments_and_restarts(H, q):
 
 
 @pytest.mark.parametrize("H", [64, 128])
+def test_first_and_last_pool_rows(H):
+    """Tables that name row 0 and the last row of both pools (and -1 slots
+    around them): every row load, including the FP8 rows' one-row buffer
+    resource, reaches exactly the pool's ends."""
+    need_gpu()
+    swa_rows, comp_rows = 600, 900
+    idx = np.full((3, 300), -1, np.int32)
+    idx[:, 0], idx[:, 1], idx[:, 127] = 0, swa_rows - 1, swa_rows - 1
+    idx[:, 128], idx[:, 129], idx[:, 299] = comp_rows - 1, 0, comp_rows - 1
+    idx[1, 130:160] = np.arange(comp_rows - 30, comp_rows)
+    idx[2, 2:40] = np.arange(swa_rows - 38, swa_rows)
+    for kv in (W.BF16, W.FP8):
+        w = custom(idx, kv=kv, q=kv, H=H, swa_rows=swa_rows, comp_rows=comp_rows)
+        check(w, what=f"pool ends H={H} kv={kv}")
+        qc = L.DTYPE_FP8_E4M3FN if kv == W.FP8 else L.DTYPE_BF16
+        check(w, plan=L.plan_splits(3, H, 300, qc, qc, num_splits=3),
+              what=f"pool ends H={H} kv={kv} S=3")
+
+
+@pytest.mark.parametrize("H", [64, 128])
 def test_padded_pool_rows(H):
     """Pool rows with a larger stride than their 512 elements: every row
     load (LDS-DMA, and for FP8 rows the per-row buffer resource) starts at
