@@ -6,8 +6,11 @@ not before inline asm, and the S^T MFMAs of the decode kernels are inline
 asm (their accumulator must stay in VGPRs).  An operand written by the VALU
 right before such an MFMA is read stale: the logits come out wrong with no
 error (whole heads turned NaN in a variant that widened its operands just
-before the MFMA).  This test compiles the kernels to gfx950 assembly and
-checks every inline-asm MFMA against the VALU writes before it.
+before the MFMA).  The other direction holds as well: the MFMA's result
+may be read by another instruction only after its passes (the kernels wait
+18 states; the compiler's own rule for this 8-pass MFMA is 11).  This test
+compiles the kernels to gfx950 assembly and checks every inline-asm MFMA
+against the VALU writes before it and the reads of its result after it.
 """
 
 import os
@@ -18,7 +21,8 @@ import pytest
 
 from sparse_mla_decode_gather_amd import build as B
 
-WAIT_STATES = 2
+WAIT_STATES = 2          # VALU write of an operand -> MFMA read
+RESULT_WAIT_STATES = 11  # 8-pass MFMA result -> read by a non-MFMA instruction
 
 
 def _vgprs(tok: str) -> set:
@@ -31,17 +35,20 @@ def _vgprs(tok: str) -> set:
 
 
 def scan(asm: str) -> tuple[int, list]:
-    """Returns (inline-asm MFMAs seen, violations).  Walks back from each
-    inline-asm MFMA over the preceding instructions in program order,
-    counting one wait state per instruction and N+1 per s_nop N."""
+    """Returns (inline-asm MFMAs seen, violations), in program order,
+    counting one wait state per instruction and N+1 per s_nop N: (1) walking
+    back from each inline-asm MFMA, no VALU write of a VGPR it reads within
+    WAIT_STATES; (2) going forward from it, no non-MFMA instruction reading
+    its result within RESULT_WAIT_STATES (MFMAs may chain on it)."""
     seen, bad = 0, []
     in_asm = False
     hist = []                      # (opcode, written VGPRs, wait states it adds)
+    pending = []                   # [result VGPRs, wait states still needed, MFMA text]
     func = "?"
     for line in asm.splitlines():
         t = line.strip()
         if re.match(r"^_Z\S+:", t):
-            func, hist = t.split(":")[0], []
+            func, hist, pending = t.split(":")[0], [], []
             continue
         if t.startswith(";;#ASMSTART"):
             in_asm = True
@@ -53,6 +60,15 @@ def scan(asm: str) -> tuple[int, list]:
             continue
         op = t.split()[0]
         args = [a.strip() for a in t[len(op):].split(",")]
+        if not op.startswith(("v_mfma", "s_")):
+            first = 0 if ("store" in op or op.startswith("ds_write")) else 1
+            reads = set()
+            for a in args[first:]:
+                reads |= _vgprs(a.split()[0]) if a else set()
+            for dst, need, mf in pending:
+                if need > 0 and dst & reads:
+                    bad.append(f"{func}: {mf} then {t} with {RESULT_WAIT_STATES - need} "
+                               f"wait state(s)")
         if op.startswith("v_mfma") and in_asm:
             seen += 1
             srcs = set()
@@ -66,6 +82,10 @@ def scan(asm: str) -> tuple[int, list]:
                     bad.append(f"{func}: {pop} then {t} after {ws} wait state(s)")
                     break
                 ws += w
+        step = (int(args[0]) + 1 if args and args[0].isdigit() else 1) if op == "s_nop" else 1
+        pending = [[d, n - step, m] for d, n, m in pending if n - step > 0]
+        if op.startswith("v_mfma") and in_asm:
+            pending.append([_vgprs(args[0].split()[0]), RESULT_WAIT_STATES, t])
         if op == "s_nop":
             n = int(args[0]) if args and args[0].isdigit() else 0
             hist.append((op, set(), n + 1))
@@ -86,7 +106,7 @@ def test_scanner_flags_a_valu_written_operand():
         "\t;;#ASMSTART",
         "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[10:13], v[20:23], v[0:15]",
         "\t;;#ASMEND",
-        "\tv_mov_b32_e32 v11, v3",
+        "\tv_mov_b32_e32 v11, v40",
         "\t;;#ASMSTART",
         "\ts_nop 1",
         "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[10:13], v[20:23], v[0:15]",
@@ -94,6 +114,25 @@ def test_scanner_flags_a_valu_written_operand():
     ])
     seen, bad = scan(snippet)
     assert seen == 2 and len(bad) == 1 and "v_cvt_scalef32" in bad[0]
+
+
+def test_scanner_flags_an_early_read_of_an_mfma_result():
+    snippet = "\n".join([
+        "_Zfake:",
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]",
+        "\ts_nop 7",
+        "\t;;#ASMEND",
+        "\tv_max_f32_e32 v30, v1, v2",
+        "\t;;#ASMSTART",
+        "\tv_mfma_f32_32x32x16_bf16 v[0:15], v[20:23], v[24:27], v[0:15]",
+        "\ts_nop 7",
+        "\ts_nop 7",
+        "\t;;#ASMEND",
+        "\tv_max_f32_e32 v30, v1, v2",
+    ])
+    seen, bad = scan(snippet)
+    assert seen == 2 and len(bad) == 1 and "v_max_f32" in bad[0]
 
 
 def test_inline_asm_mfma_operands_have_their_wait_states(tmp_path):
