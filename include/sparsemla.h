@@ -87,7 +87,13 @@ typedef struct ihipStream_t* smla_stream_t;
  * the resolved plan {head_tiles, num_splits, chunks_per_block}).  Table
  * columns are cut into chunks of chunk_cols; split s covers columns
  * [s*chunks_per_split*chunk_cols, (s+1)*chunks_per_split*chunk_cols).  A
- * split whose columns are all inactive yields an empty partial. */
+ * split whose columns are all inactive yields an empty partial.  A plan
+ * passed to a decode call must have 1 <= num_splits <= SMLA_MAX_SPLITS,
+ * chunk_cols and chunks_per_split >= 1, K equal to the call's K, and span
+ * num_splits * chunks_per_split * chunk_cols columns with
+ * K <= span <= SMLA_MAX_PLAN_COLUMNS; otherwise the call returns
+ * SMLA_ERR_BAD_PLAN. */
+#define SMLA_MAX_PLAN_COLUMNS (1 << 30)
 typedef struct smla_plan {
   int32_t num_splits;        /* S >= 1; S == 1 writes out/out_lse directly */
   int32_t head_tiles;        /* always 1: one workgroup covers all heads */
@@ -128,9 +134,11 @@ typedef struct smla_decode_args {
   int32_t num_requests;
   int32_t reserved0;
   const float* sinks;          /* [H] fp32 or NULL */
-  float bmm1_scale;            /* QK scale: sm_scale (* q_scale * kv_scale for FP8) */
-  float bmm2_scale;            /* VO scale: 1 (or kv_scale for FP8 pools) */
-  float lse_scale;             /* multiplier of the base-2 LSE, 1 by default */
+  float bmm1_scale;            /* QK scale: sm_scale (* q_scale * kv_scale for FP8);
+                                  must be finite and > 0 (a softmax scale), and
+                                  bmm1_scale * log2(e) must be a finite float */
+  float bmm2_scale;            /* VO scale: 1 (or kv_scale for FP8 pools); finite */
+  float lse_scale;             /* multiplier of the base-2 LSE, 1 by default; finite */
   int32_t reserved1;
   void* out;                   /* [T, H, 512] BF16 contiguous, 16-B aligned */
   float* out_lse;              /* [T, H] fp32 or NULL */
@@ -147,7 +155,8 @@ typedef struct smla_decode_args {
  *   forces S = clamp(override, 1, min(num_chunks, SMLA_MAX_SPLITS));
  *   num_cus <= 0 queries the current device's compute-unit count once and
  *   caches it per device.
- * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1 or a NULL out_plan,
+ * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1, K > SMLA_MAX_PLAN_COLUMNS
+ * or a NULL out_plan,
  * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128}, SMLA_ERR_HIP if the
  * device query fails. */
 int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
@@ -176,7 +185,8 @@ int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
  * launches).  Alignment rules (SMLA_ERR_MISALIGNED): q, out, both pools
  * and pool_row_stride * element size are multiples of 16 bytes; the
  * workspace is 256-B aligned.  Indices at columns >= topk_lens[t] are
- * never read as rows. */
+ * never read as rows.  A bmm1_scale that is not a positive finite number,
+ * or a non-finite bmm2_scale or lse_scale, gives SMLA_ERR_INVALID_ARG. */
 int sparse_mla_decode(const smla_decode_args* args, const smla_plan* plan,
                       smla_stream_t stream);
 
@@ -339,7 +349,8 @@ int sparse_mla_gather_only(const smla_decode_args* args, const smla_plan* plan,
                            smla_stream_t stream);
 
 /* Merge split partials (FlashInfer cake_* "mid_out"/"mid_lse" and the
- * combine of msa_sparse_decode_attention "force_fused"):
+ * combine of msa_sparse_decode_attention "force_fused"; a non-finite
+ * lse_scale gives SMLA_ERR_INVALID_ARG):
  *   mid_out [T, H, split_stride, 512] BF16 and mid_lse [T, H, split_stride]
  *   fp32 hold, for splits s < S, a normalised partial output (bmm2 already
  *   applied) and its base-2 LSE without sink or lse_scale (-inf = empty).

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -76,12 +77,28 @@ Layout layout_for(int S, int T, int H, int flags) {
   return L;
 }
 
+// Largest number of table columns a plan may span (num_splits x columns per
+// split).  The kernels form column numbers s * split_cols + c in 32-bit
+// ints, a table segment past the last one included, so the span stays far
+// below INT_MAX.
+constexpr int64_t kMaxPlanColumns = SMLA_MAX_PLAN_COLUMNS;
+
 bool plan_ok(const smla_plan* p, int K) {
   if (p->num_splits < 1 || p->num_splits > SMLA_MAX_SPLITS) return false;
   if (p->chunk_cols < 1 || p->chunks_per_split < 1) return false;
   if (p->K != K) return false;
-  const int64_t cover = (int64_t)p->num_splits * p->chunks_per_split * p->chunk_cols;
-  return cover >= K;
+  const int64_t split_cols = (int64_t)p->chunks_per_split * p->chunk_cols;
+  const int64_t cover = split_cols * p->num_splits;
+  return cover >= K && cover <= kMaxPlanColumns;
+}
+
+// The QK scale must be a positive finite number (the kernels take the max of
+// the raw logits and scale it afterwards, which needs a positive scale, and
+// bmm1_scale * log2(e) must stay finite); the other scales must be finite.
+bool scales_ok(float bmm1, float bmm2, float lse_scale) {
+  const double s1 = (double)bmm1 * 1.4426950408889634;
+  return std::isfinite(bmm1) && bmm1 > 0.f && s1 <= (double)FLT_MAX &&
+         std::isfinite(bmm2) && std::isfinite(lse_scale);
 }
 
 }  // namespace
@@ -91,7 +108,7 @@ extern "C" {
 int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
                            int max_splits, int num_splits_override,
                            int num_cus, smla_plan* out_plan) {
-  if (!out_plan || T < 0 || K < 1) return SMLA_ERR_INVALID_ARG;
+  if (!out_plan || T < 0 || K < 1 || K > kMaxPlanColumns) return SMLA_ERR_INVALID_ARG;
   if (H != 64 && H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (!dtype_pair_ok(q_dtype, kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
   if (num_cus <= 0) {
@@ -177,6 +194,8 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
   if (a->H != 64 && a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (!dtype_pair_ok(a->q_dtype, a->kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
+  if (with_outputs && !scales_ok(a->bmm1_scale, a->bmm2_scale, a->lse_scale))
+    return SMLA_ERR_INVALID_ARG;
   // the two tables: widths, rows, strides (in elements)
   int k1, k2;
   const int32_t *t1, *t2;
@@ -426,7 +445,8 @@ int sparse_mla_combine(const void* mid_out, const float* mid_lse, int T, int H,
                        int S, int split_stride, const float* sinks,
                        float lse_scale, void* out, float* out_lse,
                        smla_stream_t stream_handle) {
-  if (T < 0 || S < 1 || S > SMLA_MAX_SPLITS || split_stride < S)
+  if (T < 0 || S < 1 || S > SMLA_MAX_SPLITS || split_stride < S ||
+      !std::isfinite(lse_scale))
     return SMLA_ERR_INVALID_ARG;
   if (H != 64 && H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (T == 0) return SMLA_OK;

@@ -30,10 +30,11 @@
 //    first tile and left alone; a tile exceeding it by more than 2^64 makes
 //    the split start over with the higher reference, so O is never rescaled
 //    and the result is exact up to rounding.
-//  * decode_kernel (H=64, and FP8 rows): wave w computes S and O for its
-//    own 32 heads.  decode_hd_kernel (H=128, BF16 rows): wave w computes S
-//    for 32 heads but O for a quarter of the output dims of all heads, with
-//    P exchanged through LDS (see there).
+//  * decode_kernel (H=64, BF16 or FP8 rows): wave w computes S and O for
+//    its own 32 heads.  decode_hd_kernel (H=128, BF16 or FP8 rows): wave w
+//    computes S for 32 heads but O for a quarter of the output dims of all
+//    heads, with P exchanged through LDS (see there).  FP8 q and FP8 rows
+//    are widened exactly to BF16 and multiplied on the BF16 MFMA.
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
 //    merges them.

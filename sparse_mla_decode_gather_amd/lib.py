@@ -195,6 +195,49 @@ def dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported element type {t.dtype}")
 
 
+def _require(ok: bool, what: str):
+    if not ok:
+        raise ValueError(what)
+
+
+def _check_tensors(q, out, out_lse, pools, tables, vectors, sinks):
+    """Layout checks of the arguments the C ABI takes as bare pointers, so
+    that a tensor whose memory does not have the layout the library reads
+    is refused here instead of being misread (the library cannot see
+    strides or dtypes).  q / out / out_lse contiguous [T,H,512] / [T,H];
+    pools [rows, 512] views with unit column stride, one dtype and one row
+    stride for both; tables int32 with unit column stride; per-token
+    vectors int32 and contiguous; sinks float32 and contiguous."""
+    _require(q.dim() == 3 and q.shape[2] == 512, "q must be [T, H, 512]")
+    _require(q.is_contiguous(), "q must be contiguous")
+    T, H = int(q.shape[0]), int(q.shape[1])
+    if out is not None:
+        _require(out.dtype == torch.bfloat16 and tuple(out.shape) == (T, H, 512)
+                 and out.is_contiguous(), "out must be a contiguous BF16 [T, H, 512]")
+    if out_lse is not None:
+        _require(out_lse.dtype == torch.float32 and tuple(out_lse.shape) == (T, H)
+                 and out_lse.is_contiguous(), "out_lse must be a contiguous fp32 [T, H]")
+    live = [p for p in pools if p is not None]
+    for p in live:
+        _require(p.dim() == 2 and p.shape[1] == 512 and p.stride(1) == 1,
+                 "pools must be [rows, 512] with unit column stride")
+    if len(live) == 2:
+        _require(live[0].dtype == live[1].dtype, "both pools must have one dtype")
+        _require(live[0].stride(0) == live[1].stride(0),
+                 "both pools must have one row stride")
+    for t in tables:
+        if t is not None:
+            _require(t.dtype == torch.int32 and t.dim() == 2 and t.stride(1) == 1,
+                     "index tables must be int32 [rows, width] with unit column stride")
+    for v in vectors:
+        if v is not None:
+            _require(v.dtype == torch.int32 and v.is_contiguous(),
+                     "per-token lengths / request vectors must be contiguous int32")
+    if sinks is not None:
+        _require(sinks.dtype == torch.float32 and sinks.is_contiguous()
+                 and sinks.numel() >= H, "sinks must be a contiguous fp32 [H]")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -245,6 +288,8 @@ def make_args(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
               topk_lens=None, seq_lens=None, cum_seq_lens_q=None, sinks=None,
               bmm1_scale=1.0, bmm2_scale=1.0, lse_scale=1.0, workspace=None,
               flags=0, pool_row_stride=0) -> DecodeArgs:
+    _check_tensors(q, out, out_lse, (swa_pool, compressed_pool), (indices,),
+                   (topk_lens, seq_lens, cum_seq_lens_q), sinks)
     a = DecodeArgs()
     T, H = int(q.shape[0]), int(q.shape[1])
     a.T, a.H, a.K = T, H, int(indices.shape[1])
@@ -313,7 +358,9 @@ def make_segments(swa_indices, extra_indices, swa_topk_lens=None,
 
 def _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, topk_lens,
                         seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
-                        lse_scale, workspace, flags) -> DecodeArgs:
+                        lse_scale, workspace, flags, tables=()) -> DecodeArgs:
+    _check_tensors(q, out, out_lse, (swa_pool, compressed_pool), tables,
+                   (topk_lens, seq_lens, cum_seq_lens_q), sinks)
     a = DecodeArgs()
     a.T, a.H, a.K = int(q.shape[0]), int(q.shape[1]), K
     a.q_dtype = dtype_code(q)
@@ -368,9 +415,11 @@ def decode_paged(q, swa_pool, compressed_pool, swa_indices, block_tables,
             swa_pool if swa_pool is not None else compressed_pool))
     if workspace is None:
         workspace = alloc_workspace(plan, T, H, flags, q.device)
+    _check_tensors(q, None, None, (), (), (swa_topk_lens, hca_seq_lens), None)
     a = _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, topk_lens,
                             seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
-                            lse_scale, workspace, flags)
+                            lse_scale, workspace, flags,
+                            tables=(swa_indices, block_tables))
     _check(load().sparse_mla_decode_paged(ctypes.byref(a), ctypes.byref(g),
                                           ctypes.byref(plan), _stream(stream)),
            "sparse_mla_decode_paged")
@@ -395,9 +444,11 @@ def decode_segments(q, swa_pool, compressed_pool, swa_indices, extra_indices, ou
             swa_pool if swa_pool is not None else compressed_pool))
     if workspace is None:
         workspace = alloc_workspace(plan, T, H, flags, q.device)
+    _check_tensors(q, None, None, (), (), (swa_topk_lens, extra_topk_lens), None)
     a = _args_without_table(q, swa_pool, compressed_pool, K, out, out_lse, None,
                             seq_lens, cum_seq_lens_q, sinks, bmm1_scale, bmm2_scale,
-                            lse_scale, workspace, flags)
+                            lse_scale, workspace, flags,
+                            tables=(swa_indices, extra_indices))
     _check(load().sparse_mla_decode_segments(ctypes.byref(a), ctypes.byref(g),
                                              ctypes.byref(plan), _stream(stream)),
            "sparse_mla_decode_segments")

@@ -67,20 +67,42 @@ def compare(out, lse, ref, tol, tokens=None, what=""):
     if tokens is not None:
         o, l = o[list(tokens)], l[list(tokens)]
     ro, rl = ref["out"], ref["lse"]
+    assert o.shape == ro.shape and l.shape == rl.shape, \
+        f"{what}: shapes {o.shape}/{l.shape} vs oracle {ro.shape}/{rl.shape}"
+    # The oracle's outputs are finite; a NaN or an infinity on the GPU side
+    # (an element never written into a NaN-filled buffer, a head that came
+    # out NaN) must fail, so the test is "not within the bound" rather than
+    # "beyond the bound" (every comparison with NaN is false).
+    assert np.all(np.isfinite(ro)), f"{what}: oracle output not finite"
     err = np.abs(o - ro)
     bound = atol + rtol * np.abs(ro)
-    bad = err > bound
+    bad = ~(err <= bound)
     if bad.any():
-        i = np.unravel_index(np.argmax(err - bound), err.shape)
+        score = np.where(bad, np.where(np.isfinite(err), err - bound, np.inf), -np.inf)
+        i = np.unravel_index(np.argmax(score), err.shape)
         raise AssertionError(
-            f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance; "
-            f"worst at {i}: gpu {o[i]!r} oracle {ro[i]!r}")
+            f"{what}: {bad.sum()} of {bad.size} outputs out of tolerance or not "
+            f"finite; worst at {i}: gpu {o[i]!r} oracle {ro[i]!r}")
+    assert not np.isnan(l).any(), f"{what}: NaN in the GPU LSE"
     assert np.array_equal(np.isneginf(l), np.isneginf(rl)), f"{what}: -inf LSE mismatch"
+    assert np.array_equal(np.isposinf(l), np.isposinf(rl)), f"{what}: +inf LSE mismatch"
     fin = np.isfinite(rl)
     lerr = np.abs(l[fin] - rl[fin])
-    assert lerr.size == 0 or lerr.max() <= LSE_ATOL, \
-        f"{what}: LSE error {lerr.max():.3g} > {LSE_ATOL}"
+    lbad = ~(lerr <= LSE_ATOL)
+    assert not lbad.any(), \
+        f"{what}: {lbad.sum()} LSEs off by more than {LSE_ATOL} (or not finite)"
     return float(err.max()), float(lerr.max()) if lerr.size else 0.0
+
+
+def same_bits(a: torch.Tensor, b: torch.Tensor, what=""):
+    """a and b hold identical bits, and a holds no NaN.  Outputs start out
+    NaN-filled, so an element no kernel wrote is NaN and must not pass as
+    equal to another unwritten element (-inf, an empty token's LSE, is a
+    value and is allowed)."""
+    assert a.shape == b.shape, f"{what}: shapes {tuple(a.shape)} vs {tuple(b.shape)}"
+    assert not torch.isnan(a.float()).any(), f"{what}: NaN (unwritten or invalid) output"
+    iv = {2: torch.int16, 4: torch.int32}[a.element_size()]
+    assert torch.equal(a.view(iv), b.view(iv)), f"{what}: bits differ"
 
 
 def run_decode(w, plan=None, flags=0, workspace=None, out_lse=True):

@@ -155,6 +155,39 @@ def test_decode_rejects(so, field, value, code):
     assert call(so, a) == code
 
 
+@pytest.mark.parametrize("field,value", [
+    ("bmm1_scale", 0.0), ("bmm1_scale", -0.04), ("bmm1_scale", float("nan")),
+    ("bmm1_scale", float("inf")), ("bmm1_scale", 3.0e38),
+    ("bmm2_scale", float("nan")), ("bmm2_scale", float("-inf")),
+    ("lse_scale", float("inf")), ("lse_scale", float("nan")),
+])
+def test_decode_rejects_bad_scales(so, field, value):
+    """The QK scale must be positive and finite (the kernels scale the raw
+    tile max, which needs a positive scale; times log2(e) it must stay a
+    finite float); the other two must be finite.  Every table form checks
+    them before anything is launched."""
+    a = good_args()
+    setattr(a, field, value)
+    assert call(so, a) == 1
+    a = seg_args()
+    setattr(a, field, value)
+    assert call_seg(so, a, good_segments()) == 1
+    a = paged_args()
+    setattr(a, field, value)
+    assert call_paged(so, a, good_paged()) == 1
+
+
+def test_decode_accepts_small_and_negative_free_scales(so):
+    """Scales that are allowed reach the plan check (forced to fail here so
+    that nothing is launched): a tiny positive bmm1, negative bmm2 and
+    lse_scale."""
+    a = good_args()
+    a.bmm1_scale, a.bmm2_scale, a.lse_scale = 1e-30, -2.0, -0.5
+    p = plan(4, 128, 256)
+    p.K = 999
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 6
+
+
 def test_decode_null_args_and_empty_batch(so):
     assert so.sparse_mla_decode(None, None, None) == 1
     a = good_args(T=0)
@@ -198,6 +231,13 @@ def test_decode_workspace_checks(so):
     lambda p: setattr(p, "chunk_cols", 0),
     lambda p: setattr(p, "K", 999),
     lambda p: setattr(p, "chunks_per_split", 1),   # no longer covers K
+    # spans that would overflow the kernels' 32-bit column numbers
+    lambda p: (setattr(p, "num_splits", 4), setattr(p, "chunk_cols", 1 << 29),
+               setattr(p, "chunks_per_split", 2)),
+    lambda p: (setattr(p, "num_splits", 64), setattr(p, "chunk_cols", 1 << 25),
+               setattr(p, "chunks_per_split", 1)),
+    lambda p: (setattr(p, "num_splits", 1), setattr(p, "chunk_cols", 2),
+               setattr(p, "chunks_per_split", (1 << 29) + 1)),
 ])
 def test_decode_rejects_bad_plan(so, mutate):
     a = good_args(T=4, K=2048)
@@ -214,6 +254,20 @@ def test_combine_rejects(so, args, code):
     T, H, S, stride = args
     assert so.sparse_mla_combine(DUMMY, DUMMY, T, H, S, stride, None, 1.0,
                                  DUMMY, None, None) == code
+
+
+def test_combine_rejects_non_finite_lse_scale(so):
+    for v in (float("nan"), float("inf")):
+        assert so.sparse_mla_combine(DUMMY, DUMMY, 4, 128, 4, 4, None, v,
+                                     DUMMY, None, None) == 1
+
+
+def test_plan_rejects_too_wide_tables(so):
+    p = L.Plan()
+    assert so.sparse_mla_plan_splits(4, 128, (1 << 30) + 1, 0, 0, 0, 0, 256,
+                                     ctypes.byref(p)) == 1
+    assert so.sparse_mla_plan_splits(4, 128, 1 << 30, 0, 0, 0, 0, 256,
+                                     ctypes.byref(p)) == 0
 
 
 def test_combine_rejects_null_and_misaligned(so):

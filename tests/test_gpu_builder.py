@@ -15,7 +15,7 @@ import oracle
 from sparse_mla_decode_gather_amd import lib as L
 from sparse_mla_decode_gather_amd import workloads as W
 
-from parity_utils import log, need_gpu, run_decode
+from parity_utils import same_bits, log, need_gpu, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -130,7 +130,7 @@ def test_built_table_feeds_the_decode_like_the_page_table_form():
                    bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
                    lse_scale=w.lse_scale, plan=plan)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    same_bits(out, out2)
     assert torch.equal(lse, lse2)
     ref_idx, ref_lens, _ = oracle.build_combined_indices(
         swa.cpu().numpy(), comp, local=True, page_size=ps, block_tables=bt,

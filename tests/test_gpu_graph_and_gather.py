@@ -9,7 +9,7 @@ import torch
 from sparse_mla_decode_gather_amd import lib as L
 from sparse_mla_decode_gather_amd import workloads as W
 
-from parity_utils import TOL_BF16, compare, log, need_gpu, oracle_for, run_decode
+from parity_utils import same_bits, TOL_BF16, compare, log, need_gpu, oracle_for, run_decode
 
 pytestmark = pytest.mark.gpu
 
@@ -50,8 +50,8 @@ def test_graph_replays_match_eager(T, splits):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), rep
-        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), rep
+        same_bits(out, ref_out, str(rep))
+        same_bits(lse, ref_lse, str(rep))
 
 
 def _replays_match_eager(call, out, lse, what):
@@ -75,8 +75,8 @@ def _replays_match_eager(call, out, lse, what):
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), (what, rep)
-        assert torch.equal(lse.view(torch.int32), ref_lse.view(torch.int32)), (what, rep)
+        same_bits(out, ref_out, str((what, rep)))
+        same_bits(lse, ref_lse, str((what, rep)))
 
 
 @pytest.mark.parametrize("form,splits", [("segments", 4), ("segments", 1),

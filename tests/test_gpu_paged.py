@@ -11,7 +11,7 @@ import torch
 import oracle
 from sparse_mla_decode_gather_amd import lib as L
 from sparse_mla_decode_gather_amd import workloads as W
-from parity_utils import TOL_BF16, TOL_FP8, compare, log, need_gpu
+from parity_utils import same_bits, TOL_BF16, TOL_FP8, compare, log, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -115,7 +115,7 @@ def test_paged_equals_the_expanded_two_segment_call_bitwise():
                           sinks=c["sinks"], bmm1_scale=c["b1"], bmm2_scale=c["b2"], plan=plan)
         torch.cuda.synchronize()
         log(f"[paged] expanded-table equality T={T} pages={pages}x{ps} H={H} kv={kv} S={S}")
-        assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
+        same_bits(a_out, b_out)
         assert torch.equal(a_lse, b_lse)
 
 
@@ -131,7 +131,7 @@ def test_paged_full_size_matches_expanded_and_sampled_oracle():
     L.decode_segments(c["q"], c["swa"], c["comp"], c["si"], expanded(c), b_out, out_lse=b_lse,
                       sinks=c["sinks"], bmm1_scale=c["b1"], bmm2_scale=c["b2"], plan=plan)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), b_out.view(torch.int16))
+    same_bits(out, b_out)
     assert torch.equal(lse, b_lse)
     toks = [0, 3, 300, 511]
     compare(out, lse, oracle_of(c, toks), TOL_BF16, toks, "paged T=512 sampled")

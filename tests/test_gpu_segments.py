@@ -11,7 +11,7 @@ import torch
 import oracle
 from sparse_mla_decode_gather_amd import lib as L
 from sparse_mla_decode_gather_amd import workloads as W
-from parity_utils import (LSE_ATOL, TOL_BF16, TOL_FP8, compare, log, need_gpu)
+from parity_utils import (same_bits, LSE_ATOL, TOL_BF16, TOL_FP8, compare, log, need_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def test_segments_equal_the_combined_table_bitwise():
                  sinks=c["sinks"], bmm1_scale=c["b1"], bmm2_scale=c["b2"], plan=plan)
         torch.cuda.synchronize()
         log(f"[segments] combined-form equality T={T} K2={K2} H={H} kv={kv} S={S}")
-        assert torch.equal(a_out.view(torch.int16), b_out.view(torch.int16))
+        same_bits(a_out, b_out)
         assert torch.equal(a_lse, b_lse)
 
 
@@ -144,7 +144,7 @@ def test_segments_full_size_matches_combined_and_sampled_oracle():
              b_out, out_lse=b_lse, sinks=c["sinks"], bmm1_scale=c["b1"],
              bmm2_scale=c["b2"], plan=plan)
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), b_out.view(torch.int16))
+    same_bits(out, b_out)
     assert torch.equal(lse, b_lse)
     toks = [0, 1, 255, 256, 511]
     compare(out, lse, oracle_of(c, toks), TOL_BF16, toks, "segments T=512 sampled")
@@ -186,5 +186,5 @@ def test_ragged_segments_batch_order_does_not_change_any_token():
         plan = L.plan_splits(T, 128, K1 + K2, num_splits=S)
         a, la = run(c, plan=plan)
         b, lb = run(cp, plan=plan)
-        assert torch.equal(a[perm].view(torch.int16), b.view(torch.int16)), S
+        same_bits(a[perm], b, str(S))
         assert torch.equal(la[perm], lb), S
