@@ -61,6 +61,8 @@ typedef struct ihipStream_t* smla_stream_t;
 #define SMLA_ERR_MISALIGNED          5  /* see the alignment rules below */
 #define SMLA_ERR_BAD_PLAN            6  /* plan fields inconsistent with the call */
 #define SMLA_ERR_HIP                 7  /* a HIP runtime call or launch failed */
+#define SMLA_ERR_TOO_LARGE           8  /* sparse_mla_decode_noalloc: the call needs
+                                           more than SMLA_NOALLOC_SCRATCH_BYTES */
 
 /* ---- element types -------------------------------------------------- */
 #define SMLA_DTYPE_BF16       0   /* bfloat16 */
@@ -189,6 +191,30 @@ int sparse_mla_workspace_layout(const smla_plan* plan, int T, int H,
  * or a non-finite bmm2_scale or lse_scale, gives SMLA_ERR_INVALID_ARG. */
 int sparse_mla_decode(const smla_decode_args* args, const smla_plan* plan,
                       smla_stream_t stream);
+
+/* Scratch bytes of sparse_mla_decode_noalloc, per GPU. */
+#define SMLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* sparse_mla_decode for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, plan, kernels and results as
+ * sparse_mla_decode, except that the caller passes no workspace
+ * (args->workspace must be NULL and args->workspace_bytes 0) and
+ * SMLA_FLAG_VALIDATE_INDICES is not offered (SMLA_ERR_INVALID_ARG
+ * otherwise).  When the plan splits, the split partials (the layout
+ * sparse_mla_workspace_size/_layout describe) go to a static device array of
+ * SMLA_NOALLOC_SCRATCH_BYTES inside the library instead; a call needing more
+ * than that returns SMLA_ERR_TOO_LARGE and launches nothing.  Each GPU the
+ * library runs on holds its own copy of that array, from the library's
+ * first use on that GPU until the process ends.  Nothing is allocated: no
+ * hipMalloc, hipFree or allocating library routine is called.  All calls on
+ * one GPU share its array, so calls that overlap in time on one GPU (on
+ * different streams, or from different threads) race and give undefined
+ * results; calls ordered on one stream are safe.  The first call on a
+ * device looks up the array's address (not a stream operation); make that
+ * first call outside graph capture.  Asynchronous on "stream". */
+int sparse_mla_decode_noalloc(const smla_decode_args* args, const smla_plan* plan,
+                              smla_stream_t stream);
 
 /* The two-segment form of the token tables (FlashInfer
  * "trtllm_batch_decode_sparse_mla_dsv4", introduction (packed-backend

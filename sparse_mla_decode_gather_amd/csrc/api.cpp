@@ -350,6 +350,36 @@ int sparse_mla_decode(const smla_decode_args* a, const smla_plan* plan,
   return launch_all(a, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
 }
 
+int sparse_mla_decode_noalloc(const smla_decode_args* a, const smla_plan* plan,
+                              smla_stream_t stream_handle) {
+  if (!a) return SMLA_ERR_INVALID_ARG;
+  // The caller brings no workspace; validation (whose error block the
+  // caller would read back through a workspace pointer) is not offered.
+  if (a->workspace != nullptr || a->workspace_bytes != 0 ||
+      (a->flags & SMLA_FLAG_VALIDATE_INDICES) != 0)
+    return SMLA_ERR_INVALID_ARG;
+  smla_decode_args b = *a;
+  smla_plan local;
+  smla::DecodeParams p;
+  Layout L;
+  // First pass with no workspace: argument checks and the layout the call
+  // needs (a call that needs none is complete right here).
+  int st = prepare_call(&b, nullptr, nullptr, plan, &local, true, &p, &L);
+  if (st == SMLA_OK) {
+    if (a->T == 0) return SMLA_OK;
+    return launch_all(&b, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
+  }
+  if (st != SMLA_ERR_WORKSPACE_TOO_SMALL) return st;
+  if (L.total > smla::kNoAllocScratchBytes) return SMLA_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  if (smla::noalloc_scratch(&scratch) != hipSuccess) return SMLA_ERR_HIP;
+  b.workspace = scratch;
+  b.workspace_bytes = smla::kNoAllocScratchBytes;
+  st = prepare_call(&b, nullptr, nullptr, plan, &local, true, &p, &L);
+  if (st != SMLA_OK) return st;
+  return launch_all(&b, plan, p, reinterpret_cast<hipStream_t>(stream_handle));
+}
+
 int sparse_mla_decode_paged(const smla_decode_args* a, const smla_paged* pg,
                             const smla_plan* plan, smla_stream_t stream_handle) {
   if (!pg) return SMLA_ERR_INVALID_ARG;
@@ -495,6 +525,9 @@ const char* sparse_mla_status_string(int status) {
     case SMLA_ERR_MISALIGNED: return "misaligned pointer or stride";
     case SMLA_ERR_BAD_PLAN: return "plan inconsistent with the call";
     case SMLA_ERR_HIP: return "HIP runtime error";
+    case SMLA_ERR_TOO_LARGE:
+      return "call needs more scratch than the allocation-free decode holds "
+             "(SMLA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

@@ -11,6 +11,9 @@ constexpr int kHeadDim = 512;
 constexpr int kSwaColumns = 128;
 constexpr int kMaxSplits = 64;
 constexpr int kErrBlockBytes = 256;
+// Scratch of the allocation-free decode, per GPU (SMLA_NOALLOC_SCRATCH_BYTES)
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
 
 // Everything the split kernel needs, resolved on the host.
 struct DecodeParams {
@@ -88,5 +91,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_gather_only(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_clear_error(int32_t* err, hipStream_t stream);
 hipError_t launch_build_indices(const BuildParams& p, hipStream_t stream);
+// Device address of the allocation-free decode's scratch on the current
+// device (kNoAllocScratchBytes, 256-B aligned); looked up once per device.
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace smla

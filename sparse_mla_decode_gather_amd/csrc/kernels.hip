@@ -42,6 +42,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace smla {
@@ -1609,7 +1611,43 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// scratch of the allocation-free decode
+// ---------------------------------------------------------------------------
+//
+// sparse_mla_decode_noalloc serves callers that cannot allocate device
+// memory: its split partials (mid_lse, mid_out) and error block live in this
+// array instead of a caller workspace.  Each GPU the library runs on holds
+// its own copy (kNoAllocScratchBytes) from the module's load until the
+// process ends.  Calls on one GPU share it, so calls that overlap on one GPU
+// race; the partials are fully written by the split kernel before the
+// combine reads them, so nothing in it has to start at zero.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
+
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept: in host code the array's name
+// is only a host-side stand-in and must never be passed to a kernel.
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream) {

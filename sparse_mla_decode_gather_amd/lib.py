@@ -22,7 +22,9 @@ STATUS = {
     0: "SMLA_OK", 1: "SMLA_ERR_INVALID_ARG", 2: "SMLA_ERR_UNSUPPORTED_DTYPE",
     3: "SMLA_ERR_UNSUPPORTED_SHAPE", 4: "SMLA_ERR_WORKSPACE_TOO_SMALL",
     5: "SMLA_ERR_MISALIGNED", 6: "SMLA_ERR_BAD_PLAN", 7: "SMLA_ERR_HIP",
+    8: "SMLA_ERR_TOO_LARGE",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3FN = 1
 FLAG_VALIDATE_INDICES = 1
@@ -135,6 +137,9 @@ def load() -> ctypes.CDLL:
     lib.sparse_mla_decode.argtypes = [ctypes.POINTER(DecodeArgs),
                                       ctypes.POINTER(Plan), ctypes.c_void_p]
     lib.sparse_mla_decode.restype = ctypes.c_int
+    lib.sparse_mla_decode_noalloc.argtypes = [ctypes.POINTER(DecodeArgs),
+                                              ctypes.POINTER(Plan), ctypes.c_void_p]
+    lib.sparse_mla_decode_noalloc.restype = ctypes.c_int
     lib.sparse_mla_decode_segments.argtypes = [
         ctypes.POINTER(DecodeArgs), ctypes.POINTER(Segments), ctypes.POINTER(Plan),
         ctypes.c_void_p]
@@ -339,6 +344,27 @@ def decode(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
                      lse_scale=lse_scale, workspace=workspace, flags=flags)
     _check(load().sparse_mla_decode(ctypes.byref(args), ctypes.byref(plan),
                                     _stream(stream)), "sparse_mla_decode")
+    return plan
+
+
+def decode_noalloc(q, swa_pool, compressed_pool, indices, out, *, out_lse=None,
+                   topk_lens=None, seq_lens=None, cum_seq_lens_q=None, sinks=None,
+                   bmm1_scale=1.0, bmm2_scale=1.0, lse_scale=1.0,
+                   plan: Optional[Plan] = None, stream=None) -> Plan:
+    """sparse_mla_decode_noalloc: sparse_mla_decode with no workspace (the
+    split partials live in the library's own static device scratch; nothing
+    is allocated here or in the library).  Writes ``out`` (and ``out_lse``)
+    in place and returns the plan used."""
+    T, H, K = int(q.shape[0]), int(q.shape[1]), int(indices.shape[1])
+    if plan is None:
+        plan = plan_splits(T, H, K, dtype_code(q), dtype_code(swa_pool))
+    args = make_args(q, swa_pool, compressed_pool, indices, out,
+                     out_lse=out_lse, topk_lens=topk_lens, seq_lens=seq_lens,
+                     cum_seq_lens_q=cum_seq_lens_q, sinks=sinks,
+                     bmm1_scale=bmm1_scale, bmm2_scale=bmm2_scale,
+                     lse_scale=lse_scale)
+    _check(load().sparse_mla_decode_noalloc(ctypes.byref(args), ctypes.byref(plan),
+                                            _stream(stream)), "sparse_mla_decode_noalloc")
     return plan
 
 

@@ -33,13 +33,13 @@ def test_every_declared_symbol_is_exported(so):
         "sparse_mla_gather_only", "sparse_mla_decode_segments",
         "sparse_mla_decode_paged", "sparse_mla_build_indices",
         "sparse_mla_combine", "sparse_mla_get_device_error",
-        "sparse_mla_status_string"}
+        "sparse_mla_status_string", "sparse_mla_decode_noalloc"}
     for n in names:
         assert hasattr(so, n), n
 
 
 def test_status_strings(so):
-    for code in range(8):
+    for code in range(9):
         assert L.status_string(code) not in ("", "unknown status")
     assert L.status_string(99) == "unknown status"
 
@@ -186,6 +186,29 @@ def test_decode_accepts_small_and_negative_free_scales(so):
     p = plan(4, 128, 256)
     p.K = 999
     assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 6
+
+
+def test_noalloc_host_checks(so):
+    """sparse_mla_decode_noalloc refuses a workspace and the validate flag,
+    and a call whose partials exceed its scratch, before any device work;
+    zero tokens do nothing."""
+    assert so.sparse_mla_decode_noalloc(None, None, None) == 1
+    a = good_args(T=512, K=2048)
+    p = plan(512, 128, 2048, override=16)
+    assert L.workspace_size(p, 512, 128) > L.NOALLOC_SCRATCH_BYTES
+    assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(p), None) == 8
+    a.workspace, a.workspace_bytes = DUMMY, 1 << 30
+    assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(p), None) == 1
+    a.workspace, a.workspace_bytes = None, 0
+    a.flags = L.FLAG_VALIDATE_INDICES
+    assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(p), None) == 1
+    a = good_args(T=0)
+    assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(plan(1, 128, 256)),
+                                        None) == 0
+    a = good_args()
+    a.bmm1_scale = 0.0
+    assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(plan(4, 128, 256)),
+                                        None) == 1
 
 
 def test_decode_null_args_and_empty_batch(so):
