@@ -21,13 +21,15 @@ form (sparse_mla_decode_segments with a 128-column SWA table and a
 rows), the combined-table builder (sparse_mla_build_indices) timed on the
 same tables expressed as request-local positions and a 64-row block table
 (it must rebuild them exactly), a cold-cache rate (a 1 GiB write between
-launches evicts L2 and MALL), and with --sweep the per-T numbers for
-T in 1, 4, 8, 64, 256, the small T also as HIP-graph replays of 20
-back-to-back launches.
+launches evicts L2 and MALL), the per-T numbers for T in 1, 4, 8, 16, 64,
+256 (the small T also as HIP-graph replays of 20 back-to-back launches),
+the other configurations (tiny, batched with sinks, FP8, speculative
+decode) with their default plans and roofline fractions, and the
+roofline fraction against peaks measured on the box.
 
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
---no-cpu-baseline, --sweep, --all-workloads (adds the other configurations:
-tiny, batched with sinks, FP8, speculative decode).
+--no-cpu-baseline, --headline-only (skip the sweep, the other
+configurations and the measured peaks), --only-workload NAME.
 """
 
 import argparse
@@ -183,10 +185,72 @@ def cpu_baseline(w, budget_s=10.0):
         secs += time.perf_counter() - t0
         done += w.T
         passes += 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(done / secs, 3), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{passes} pass(es) over all {w.T} tokens of the same "
                       f"workload (NumPy float64 oracle, {secs:.1f} s)"}
+
+
+def measured_peaks(stream):
+    """Attainable peaks on this machine, for the fractions against measured
+    rather than published peaks: streaming HBM rates of library kernels
+    (torch's sum and row sums over 4 GiB, one read pass each, and a 2 GiB
+    copy counted as read + write) and dense BF16 GEMMs of 8192^3 on N(0,1)
+    data (torch.matmul), each the best of several timed runs."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    y = torch.empty(1 << 29, dtype=torch.float32, device="cuda")
+    rows = x.view(1 << 18, 4096)
+
+    def best_ms(fn, n=8):
+        best = float("inf")
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, a.elapsed_time(b))
+        return best
+    rates = {
+        "sum": x.numel() * 4 / (best_ms(lambda: x.sum()) * 1e-3) / 1e9,
+        "row_sums": x.numel() * 4 / (best_ms(lambda: rows.sum(1)) * 1e-3) / 1e9,
+        # a copy moves its bytes twice (read + write)
+        "copy": 2 * y.numel() * 4 / (best_ms(lambda: y.copy_(x[: 1 << 29])) * 1e-3) / 1e9,
+    }
+    rd_gbps = max(rates.values())
+    del x, y, rows
+    g = torch.Generator(device="cuda").manual_seed(5)
+    n = 8192
+    A = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    B = torch.randn((n, n), device="cuda", generator=g).to(torch.bfloat16)
+    for _ in range(3):
+        A @ B
+    best_mm = float("inf")
+    for _ in range(10):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        A @ B
+        b.record(stream)
+        torch.cuda.synchronize()
+        best_mm = min(best_mm, a.elapsed_time(b))
+    del A, B
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(rd_gbps, 1),
+            "hbm_by_kernel_GBps": {k: round(v, 1) for k, v in rates.items()},
+            "bf16_gemm_TFLOPs": round(2.0 * n ** 3 / (best_mm * 1e-3) / 1e12, 1),
+            "how": "HBM: the best of torch's sum and row sums over 4 GiB fp32 and a "
+                   "2 GiB copy (read + write bytes), 8 runs each; MFMA: best of 10 "
+                   "bf16 8192^3 torch.matmul on N(0,1) data"}
 
 
 MFMA_PEAK_BY_ROWS = {"bf16": MFMA_BF16_PEAK_TFLOPS, "fp8_e4m3fn": MFMA_BF16_PEAK_TFLOPS}
@@ -247,13 +311,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--T", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true")
-    ap.add_argument("--all-workloads", action="store_true",
-                    help="also time the other configurations (tiny, batched "
-                         "with sinks, FP8, speculative decode) with their "
-                         "default plans")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the T sweep, the other configurations and the "
+                         "measured peaks (a short command to run under a "
+                         "profiler); by default the line carries all of them")
     ap.add_argument("--only-workload", choices=WORKLOAD_NAMES,
-                    help="time only this other configuration (as --all-workloads "
+                    help="time only this other configuration (as the default line "
                          "does) and print its record instead of the headline "
                          "line: a short command to run under a kernel tracer")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -376,6 +439,13 @@ def main():
         "unit": "GB/s" if bound == "hbm" else "TFLOP/s",
         "frac": round(t_roof / (avg_launch_ms * 1e-3), 4),
         "traffic": measured_traffic(),
+        # achieved / frac divide by the average launch duration (HIP events
+        # around each launch); the same on the whole timed region
+        # (ms_per_step, which also holds the gaps between launches):
+        "time_basis": "avg_launch_ms",
+        "achieved_per_step": round((gathered / (ms_step * 1e-3) / 1e9) if bound == "hbm"
+                                   else flops / (ms_step * 1e-3) / 1e12, 1),
+        "frac_per_step": round(t_roof / (ms_step * 1e-3), 4),
     }
     result = {
         "metric": "decode tokens/s + gathered-KV GB/s, H=128 topk=2048 bf16; "
@@ -413,9 +483,9 @@ def main():
                                             / HBM_PEAK_GBPS, 4),
                           "rebuilds_the_table": build_ok},
     }
-    if args.sweep:
+    if not args.headline_only:
         sweep = {}
-        for t in (1, 4, 8, 64, 256):
+        for t in (1, 4, 8, 16, 64, 256):
             if t > T:
                 continue
             p = lib.plan_splits(t, w.H, w.K)
@@ -436,13 +506,18 @@ def main():
                              "num_splits": p.num_splits,
                              "roofline_frac": round(g / (HBM_PEAK_GBPS * 1e9) /
                                                     (avg * 1e-3), 4)}
-            if t <= 8:
+            if t <= 16:
                 gms = time_graph(st)
                 sweep[str(t)]["graph_launch_us"] = round(gms * 1e3, 2)
                 sweep[str(t)]["graph_gathered_GBps"] = round(g / (gms * 1e-3) / 1e9, 1)
         result["sweep"] = sweep
-    if args.all_workloads:
+    if not args.headline_only:
         result["workloads"] = other_workloads(stream)
+        peaks = measured_peaks(stream)
+        roofline["measured_peaks"] = peaks
+        t_meas = max(gathered / (peaks["hbm_read_GBps"] * 1e9),
+                     flops / (peaks["bf16_gemm_TFLOPs"] * 1e12))
+        roofline["frac_vs_measured_peaks"] = round(t_meas / (avg_launch_ms * 1e-3), 4)
     if args.calibration_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1)
         dst = torch.empty_like(src)
