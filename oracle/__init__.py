@@ -9,7 +9,9 @@ Everything is plain NumPy in float64 (the pages fix no precision), written
 from the method's definition as the FlashInfer and vLLM pages state it:
 
 * ``formats``  - the BF16 and OCP FP8 E4M3FN bit formats, decoded from their
-  definitions, plus BF16 round-to-nearest-even for comparing rounded outputs.
+  definitions, the 584-byte packed block-scaled FP8 row (a reading of the
+  pages, see there), plus BF16 round-to-nearest-even for comparing rounded
+  outputs.
 * ``sparse_mla`` - the decode itself (selection, gather, sink-aware softmax,
   base-2 LSE), its split form and the LSE combine.
 * ``brute``    - a second, independent formulation (multiset of pool rows,
@@ -23,7 +25,7 @@ docstring says "parity unpinned".
 """
 
 from .formats import bf16_bits_to_f64, e4m3fn_bits_to_f64, decode_bits, \
-    round_to_bf16
+    round_to_bf16, ue8m0_to_f64, packed584_to_f64, PACKED_ROW_BYTES
 from .sparse_mla import (SWA_COLUMNS, active_slots, active_slots_segments,
                          active_slots_paged, decode_token, sparse_mla_decode,
                          sparse_mla_decode_segments, sparse_mla_decode_paged,
@@ -34,6 +36,7 @@ from .index_builder import build_combined_indices
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3fn_bits_to_f64", "decode_bits", "round_to_bf16",
+    "ue8m0_to_f64", "packed584_to_f64", "PACKED_ROW_BYTES",
     "SWA_COLUMNS", "active_slots", "active_slots_segments",
     "active_slots_paged", "decode_token", "sparse_mla_decode",
     "sparse_mla_decode_segments", "sparse_mla_decode_paged", "split_partials",

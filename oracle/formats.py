@@ -15,7 +15,9 @@ The encodings below are the public definitions of those two types:
   magnitude is 1.75 * 2^8 = 448.
 
 Pinned by tests/test_oracle_formats.py (closed-form landmark values and all
-256 E4M3FN codes / a sweep of BF16 codes against torch's own casts).
+256 E4M3FN codes / a sweep of BF16 codes against torch's own casts) and, for
+the packed block-scaled row, tests/test_oracle_packed.py (every UE8M0 code,
+hand-assembled rows, and the decode against the plain definition).
 """
 
 from __future__ import annotations
@@ -53,12 +55,58 @@ def e4m3fn_bits_to_f64(bits) -> np.ndarray:
     return _E4M3FN[np.asarray(bits, dtype=np.uint8)]
 
 
+# The packed block-scaled FP8 row.  FlashInfer
+# ``trtllm_batch_decode_sparse_mla_dsv4`` (introduction, packed-backend
+# paragraph; parameter ``swa_kv_cache``) gives only its size, 584 bytes per
+# token of uint8, and vLLM ``DeepseekV4FlashInferMLAAttention`` (the class
+# comment on ``use_flashmla_fp8_layout``) its family, UE8M0 block-scaled FP8.
+# Reading (the pages leave the byte order open): the row holds the 512 dims
+# in the order the query lays them out (448 NoPE, then 64 RoPE, per the Cake
+# page's ``q`` parameter), then its scales --
+#   bytes [0, 448)   : NoPE dims 0..447 as OCP E4M3FN codes,
+#   bytes [448, 576) : RoPE dims 448..511 as BF16, little-endian,
+#   bytes [576, 584) : eight UE8M0 scale bytes; byte j scales NoPE dims
+#                      [56 j, 56 j + 56) (448 = 8 x 56 uses every byte),
+# and NoPE dim d decodes to E4M3FN(byte d) * 2^(scale[d // 56] - 127).
+PACKED_ROW_BYTES = 584
+PACKED_NOPE_DIMS = 448
+PACKED_BLOCK_DIMS = 56
+PACKED_ROPE_OFFSET = 448
+PACKED_SCALE_OFFSET = 576
+
+
+def ue8m0_to_f64(codes) -> np.ndarray:
+    """UE8M0 scale bytes (an 8-bit biased exponent with no sign and no
+    mantissa, bias 127) -> exact float64 powers of two 2^(e - 127); the
+    all-ones byte 255 is NaN."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    out = np.ldexp(np.ones(e.shape), e - 127)
+    return np.where(e == 255, np.nan, out)
+
+
+def packed584_to_f64(bits) -> np.ndarray:
+    """[..., 584] uint8 packed rows -> [..., 512] exact float64 values."""
+    b = np.asarray(bits, dtype=np.uint8)
+    if b.shape[-1] != PACKED_ROW_BYTES:
+        raise ValueError(f"packed rows have {PACKED_ROW_BYTES} bytes, got {b.shape[-1]}")
+    nope = e4m3fn_bits_to_f64(b[..., :PACKED_NOPE_DIMS])
+    scale = ue8m0_to_f64(b[..., PACKED_SCALE_OFFSET:PACKED_ROW_BYTES])
+    nope = nope * np.repeat(scale, PACKED_BLOCK_DIMS, axis=-1)
+    lo = b[..., PACKED_ROPE_OFFSET:PACKED_SCALE_OFFSET:2].astype(np.uint16)
+    hi = b[..., PACKED_ROPE_OFFSET + 1:PACKED_SCALE_OFFSET:2].astype(np.uint16)
+    rope = bf16_bits_to_f64(lo | (hi << np.uint16(8)))
+    return np.concatenate([nope, rope], axis=-1)
+
+
 def decode_bits(bits, dtype: str) -> np.ndarray:
-    """Decode stored patterns of ``dtype`` ("bf16" or "fp8_e4m3fn")."""
+    """Decode stored patterns of ``dtype`` ("bf16", "fp8_e4m3fn", or
+    "packed_fp8_584" for [..., 584]-byte packed rows)."""
     if dtype == "bf16":
         return bf16_bits_to_f64(bits)
     if dtype == "fp8_e4m3fn":
         return e4m3fn_bits_to_f64(bits)
+    if dtype == "packed_fp8_584":
+        return packed584_to_f64(bits)
     raise ValueError(f"unknown dtype {dtype!r}")
 
 

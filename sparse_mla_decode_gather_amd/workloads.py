@@ -44,6 +44,11 @@ E4M3_MAX = 448.0
 
 BF16 = "bf16"
 FP8 = "fp8_e4m3fn"
+PACKED = "packed_fp8_584"   # 584-byte rows: 448 E4M3FN + 64 BF16 + 8 UE8M0 bytes
+
+PACKED_ROW_BYTES = 584
+PACKED_BLOCKS = 8           # UE8M0 scale bytes per row, one per 56 NoPE dims
+PACKED_BLOCK_DIMS = 56
 
 
 @dataclass
@@ -122,6 +127,49 @@ def normal_rows(rows: int, seed: int, device="cpu", dtype: str = BF16,
                 torch.float8_e4m3fn)
         del x
     return out
+
+
+def packed_rows(rows: int, seed: int, device="cpu", chunk_rows: int = 1 << 17,
+                spread: int = 8) -> torch.Tensor:
+    """[rows, 584] uint8 packed block-scaled FP8 rows, written the way a KV
+    cache writer would fill them (the layout the library and the oracle read:
+    bytes 0..447 E4M3FN NoPE codes, 448..575 the 64 RoPE dims as BF16,
+    576..583 one UE8M0 scale byte per 56 NoPE dims).  Values are N(0,1),
+    each 56-dim NoPE block multiplied by a seeded 2^k, k uniform in
+    [-spread, spread], so the scale bytes vary; a block's scale is the
+    smallest power of two 2^(e-127) with max|x| / 2^(e-127) <= 448, and its
+    codes are torch's float8_e4m3fn cast of x / 2^(e-127)."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty((rows, PACKED_ROW_BYTES), dtype=torch.uint8, device=device)
+    nope = PACKED_BLOCKS * PACKED_BLOCK_DIMS
+    for r0 in range(0, rows, chunk_rows):
+        r1 = min(rows, r0 + chunk_rows)
+        n = r1 - r0
+        x = torch.randn((n, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+        k = torch.randint(-spread, spread + 1, (n, PACKED_BLOCKS, 1), generator=g,
+                          device=device).float()
+        blocks = x[:, :nope].view(n, PACKED_BLOCKS, PACKED_BLOCK_DIMS) * torch.exp2(k)
+        amax = blocks.abs().amax(-1, keepdim=True).clamp_min(2.0 ** -100)
+        e = (torch.ceil(torch.log2(amax / E4M3_MAX)) + 127).clamp_(1, 254)
+        codes = (blocks / torch.exp2(e - 127)).clamp_(-E4M3_MAX, E4M3_MAX).to(
+            torch.float8_e4m3fn).view(torch.uint8)
+        out[r0:r1, :nope] = codes.reshape(n, nope)
+        out[r0:r1, nope:nope + 128] = x[:, nope:].to(torch.bfloat16).contiguous().view(
+            torch.uint8).view(n, 128)
+        out[r0:r1, nope + 128:] = e.view(n, PACKED_BLOCKS).to(torch.uint8)
+        del x, blocks, codes
+    return out
+
+
+def pool_rows(rows: int, seed: int, device="cpu", dtype: str = BF16,
+              scale: float = 1.0) -> torch.Tensor:
+    """A KV pool of ``rows`` rows in ``dtype`` (see normal_rows and
+    packed_rows)."""
+    if dtype == PACKED:
+        return packed_rows(rows, seed, device)
+    return normal_rows(rows, seed, device, dtype, scale)
 
 
 def _distinct(g: torch.Generator, n: int, k: int) -> torch.Tensor:
@@ -258,9 +306,8 @@ def _decode_batch(name, seed, device, B, q_len, H, K, seq_lo, seq_hi,
     q = normal_rows(T * H, seed * 1000 + 1, device, q_dtype,
                     scale=q_scale).view(T, H, HEAD_DIM)
     if pools:
-        swa = normal_rows(swa_rows, seed * 1000 + 2, device, kv_dtype, kv_scale)
-        comp = normal_rows(comp_rows, seed * 1000 + 3, device, kv_dtype,
-                           kv_scale)
+        swa = pool_rows(swa_rows, seed * 1000 + 2, device, kv_dtype, kv_scale)
+        comp = pool_rows(comp_rows, seed * 1000 + 3, device, kv_dtype, kv_scale)
     else:
         swa = comp = None
     qs = q_scale if q_dtype == FP8 else 1.0
@@ -326,6 +373,18 @@ def make_spec_decode(device="cpu", seed: int = 5, B: int = 256,
                          share=0.9, kv_scale=0.08, pools=pools)
 
 
+def make_packed(T: int = 512, device="cpu", seed: int = 6, H: int = 128,
+                pools=True) -> Workload:
+    """The long-context decode shape (H heads, topk 2048 = 128 SWA + 1920
+    compressed rows, seq_len 131072, sinks) with both pools in the 584-byte
+    packed block-scaled FP8 row and BF16 q; bmm1 = sm_scale, bmm2 = 1 (the
+    scales are inside the rows)."""
+    return _decode_batch(f"packed_T{T}_H{H}", seed, device, B=T, q_len=1, H=H,
+                         K=2048, seq_lo=0, seq_hi=0, q_dtype=BF16,
+                         kv_dtype=PACKED, topk_lo=2048, topk_hi=2048,
+                         fixed_seq=131072, pools=pools)
+
+
 CONFIGS = {
     "tiny": make_tiny,
     "batched_sinks": make_batched_sinks,
@@ -345,4 +404,6 @@ def raw_bits(x: torch.Tensor):
         return x.view(torch.int16).numpy().view("uint16")
     if x.dtype == torch.float8_e4m3fn:
         return x.view(torch.uint8).numpy()
+    if x.dtype == torch.uint8:          # packed rows: already bytes
+        return x.numpy()
     raise TypeError(f"unsupported dtype {x.dtype}")
