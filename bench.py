@@ -24,8 +24,9 @@ same tables expressed as request-local positions and a 64-row block table
 launches evicts L2 and MALL), the per-T numbers for T in 1, 4, 8, 16, 64,
 256 (the small T also as HIP-graph replays of 20 back-to-back launches),
 the other configurations (tiny, batched with sinks, FP8, speculative
-decode) with their default plans and roofline fractions, and the
-roofline fraction against peaks measured on the box.
+decode, and the long-context shape with packed 584-byte block-scaled FP8
+rows) with their default plans and roofline fractions, and the roofline
+fraction against peaks measured on the box.
 
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
 --no-cpu-baseline, --headline-only (skip the sweep, the other
@@ -253,10 +254,12 @@ def measured_peaks(stream):
                    "bf16 8192^3 torch.matmul on N(0,1) data"}
 
 
-MFMA_PEAK_BY_ROWS = {"bf16": MFMA_BF16_PEAK_TFLOPS, "fp8_e4m3fn": MFMA_BF16_PEAK_TFLOPS}
+MFMA_PEAK_BY_ROWS = {"bf16": MFMA_BF16_PEAK_TFLOPS, "fp8_e4m3fn": MFMA_BF16_PEAK_TFLOPS,
+                     "packed_fp8_584": MFMA_BF16_PEAK_TFLOPS}
+ROW_BYTES_BY_KV = {"bf16": 1024, "fp8_e4m3fn": 512, "packed_fp8_584": 584}
 
 
-WORKLOAD_NAMES = ("tiny", "batched_sinks", "fp8", "spec_decode")
+WORKLOAD_NAMES = ("tiny", "batched_sinks", "fp8", "spec_decode", "packed")
 
 
 def other_workloads(stream, only=None):
@@ -269,12 +272,13 @@ def other_workloads(stream, only=None):
     from sparse_mla_decode_gather_amd import lib, workloads as W
     res = {}
     for name, make in (("tiny", W.make_tiny), ("batched_sinks", W.make_batched_sinks),
-                       ("fp8", W.make_fp8), ("spec_decode", W.make_spec_decode)):
+                       ("fp8", W.make_fp8), ("spec_decode", W.make_spec_decode),
+                       ("packed", lambda dev: W.make_packed(512, dev))):
         if only is not None and name != only:
             continue
         w = make("cuda")
         n = active_slots_per_token(w)
-        rb = 1024 if w.kv_dtype == W.BF16 else 512
+        rb = ROW_BYTES_BY_KV[w.kv_dtype]
         gathered = int(n.sum()) * rb
         flops = 4.0 * 512 * w.H * int(n.sum())
         out = torch.empty((w.T, w.H, 512), dtype=torch.bfloat16, device="cuda")

@@ -55,7 +55,8 @@ typedef struct ihipStream_t* smla_stream_t;
 /* ---- status codes --------------------------------------------------- */
 #define SMLA_OK                      0
 #define SMLA_ERR_INVALID_ARG         1  /* null pointer, bad size or stride */
-#define SMLA_ERR_UNSUPPORTED_DTYPE   2  /* dtype pair not BF16/BF16, FP8/FP8, BF16/FP8 */
+#define SMLA_ERR_UNSUPPORTED_DTYPE   2  /* dtype pair (q/kv) not BF16/BF16, FP8/FP8,
+                                           BF16/FP8 or BF16/PACKED_FP8_584 */
 #define SMLA_ERR_UNSUPPORTED_SHAPE   3  /* H not 64 or 128 */
 #define SMLA_ERR_WORKSPACE_TOO_SMALL 4
 #define SMLA_ERR_MISALIGNED          5  /* see the alignment rules below */
@@ -67,6 +68,23 @@ typedef struct ihipStream_t* smla_stream_t;
 /* ---- element types -------------------------------------------------- */
 #define SMLA_DTYPE_BF16       0   /* bfloat16 */
 #define SMLA_DTYPE_FP8_E4M3FN 1   /* OCP FP8 E4M3FN, per-tensor scaled */
+/* KV pools only, with BF16 q: packed block-scaled FP8 rows of 584 bytes
+ * (FlashInfer trtllm_batch_decode_sparse_mla_dsv4, introduction,
+ * packed-backend paragraph and parameter "swa_kv_cache": 584 bytes per token
+ * of uint8; vLLM DeepseekV4FlashInferMLAAttention, class comment on
+ * use_flashmla_fp8_layout: UE8M0 block-scaled FP8).  The byte order is this
+ * library's reading, the pages giving only size and family:
+ *   bytes [0, 448)   NoPE dims 0..447 as OCP E4M3FN codes,
+ *   bytes [448, 576) RoPE dims 448..511 as BF16, little-endian,
+ *   bytes [576, 584) 8 UE8M0 scale bytes e_j (2^(e_j - 127)), byte j
+ *                    scaling NoPE dims [56 j, 56 j + 56).
+ * Scale bytes 1..254 with every scaled NoPE value in BF16's normal range
+ * are decoded exactly; 0 (2^-127) and 255 (NaN) are accepted as their UE8M0
+ * values but lie outside the tested range.  The row stride
+ * (pool_row_stride) is counted in bytes, 0 meaning 584, and must be a
+ * multiple of 8. */
+#define SMLA_DTYPE_PACKED_FP8_584 2
+#define SMLA_PACKED_ROW_BYTES 584
 
 /* ---- flags ---------------------------------------------------------- */
 /* Check every active index on the device and record the first violation
@@ -121,10 +139,11 @@ typedef struct smla_decode_args {
   const void* compressed_pool; /* [compressed_rows, row_stride]; may be NULL
                                   only if K <= 128 */
   int64_t compressed_rows;
-  int32_t kv_dtype;            /* dtype of both pools */
+  int32_t kv_dtype;            /* dtype of both pools (SMLA_DTYPE_*) */
   int32_t flags;               /* SMLA_FLAG_* */
   int64_t pool_row_stride;     /* elements between rows of both pools; 0 means
-                                  512.  A pool of one KV head is the same
+                                  512 (bytes, and 0 means 584, for
+                                  SMLA_DTYPE_PACKED_FP8_584 rows).  A pool of one KV head is the same
                                   bytes in HND and NHD layouts, so a paged
                                   [pages, page_size, 512] pool is passed as
                                   flat rows row = page * page_size + offset */

@@ -153,7 +153,8 @@ def active_slots_paged(swa_row, swa_len: Optional[int], block_row,
 def gather_rows(slots, swa_bits, comp_bits, kv_dtype: str) -> np.ndarray:
     """Decoded float64 rows [n, 512] for the given active slots."""
     if not slots:
-        return np.zeros((0, swa_bits.shape[1]), dtype=np.float64)
+        # no rows: the decoded width (512 for every row format)
+        return decode_bits(np.asarray(swa_bits)[:0], kv_dtype)
     rows = []
     for _, pool, r in slots:
         src = swa_bits if pool == 0 else comp_bits

@@ -49,6 +49,7 @@ int query_cu_count(int* out) {
 
 bool dtype_pair_ok(int q, int kv) {
   if (q == SMLA_DTYPE_BF16 && kv == SMLA_DTYPE_BF16) return true;
+  if (q == SMLA_DTYPE_BF16 && kv == SMLA_DTYPE_PACKED_FP8_584) return true;
   if (q == SMLA_DTYPE_FP8_E4M3FN && kv == SMLA_DTYPE_FP8_E4M3FN) return true;
   if (q == SMLA_DTYPE_BF16 && kv == SMLA_DTYPE_FP8_E4M3FN) return true;
   return false;
@@ -127,8 +128,9 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     // Workgroups resident per CU: one at H=128 (it holds 32 heads of O per
     // wave in registers), two at H=64.
     const int64_t slots = (int64_t)num_cus * (H == 64 ? 2 : 1);
-    // Per-row cost relative to a BF16 row: FP8 rows move half the bytes.
-    const int64_t row_w = (kv_dtype == SMLA_DTYPE_FP8_E4M3FN) ? 1 : 2;
+    // Per-row cost relative to a BF16 row: FP8 rows (512 B) and packed rows
+    // (584 B) move about half the bytes.
+    const int64_t row_w = (kv_dtype == SMLA_DTYPE_BF16) ? 2 : 1;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {
       const int64_t cps = (num_chunks + s - 1) / s;
@@ -243,14 +245,22 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   if (k2 > 0 && (!t2 || !a->compressed_pool || s2 < t2_width)) return SMLA_ERR_INVALID_ARG;
   if (a->swa_rows < 0 || a->compressed_rows < 0) return SMLA_ERR_INVALID_ARG;
   if ((int64_t)a->T * a->H > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
-  const int64_t row_stride = a->pool_row_stride == 0 ? smla::kHeadDim : a->pool_row_stride;
-  if (row_stride < smla::kHeadDim) return SMLA_ERR_INVALID_ARG;
+  // A pool row is 512 elements, or 584 bytes for packed rows (its stride is
+  // then counted in bytes).
+  const bool packed = a->kv_dtype == SMLA_DTYPE_PACKED_FP8_584;
+  const int64_t row_elems = packed ? SMLA_PACKED_ROW_BYTES : smla::kHeadDim;
+  const int64_t row_stride = a->pool_row_stride == 0 ? row_elems : a->pool_row_stride;
+  if (row_stride < row_elems) return SMLA_ERR_INVALID_ARG;
   if (a->cum_seq_lens_q && a->num_requests < 1) return SMLA_ERR_INVALID_ARG;
-  const int kv_elem = a->kv_dtype == SMLA_DTYPE_FP8_E4M3FN ? 1 : 2;
+  const int kv_elem = a->kv_dtype == SMLA_DTYPE_BF16 ? 2 : 1;
+  // rows start 16-B aligned (8-B for packed rows, whose loads are 8 and 16
+  // bytes at 4-byte aligned offsets)
+  const int64_t row_align = packed ? 8 : 16;
   if (!aligned(a->q, 16) || (with_outputs && !aligned(a->out, 16)) ||
       (a->swa_pool && !aligned(a->swa_pool, 16)) ||
       (a->compressed_pool && !aligned(a->compressed_pool, 16)) ||
-      (row_stride * kv_elem) % 16 != 0 || (t1 && !aligned(t1, 4)) || (t2 && !aligned(t2, 4)))
+      (row_stride * kv_elem) % row_align != 0 || (t1 && !aligned(t1, 4)) ||
+      (t2 && !aligned(t2, 4)))
     return SMLA_ERR_MISALIGNED;
 
   if (!plan) {

@@ -11,6 +11,9 @@ constexpr int kHeadDim = 512;
 constexpr int kSwaColumns = 128;
 constexpr int kMaxSplits = 64;
 constexpr int kErrBlockBytes = 256;
+// kv dtype code of the 584-byte packed block-scaled FP8 rows
+// (SMLA_DTYPE_PACKED_FP8_584)
+constexpr int kKvPacked584 = 2;
 // Scratch of the allocation-free decode, per GPU (SMLA_NOALLOC_SCRATCH_BYTES)
 constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
 constexpr int kMaxDevices = 64;

@@ -233,6 +233,96 @@ __device__ __forceinline__ u32x2 load_row8(const uint8_t* row, uint32_t off) {
 }
 typedef int32_t __attribute__((address_space(1))) global_i32;
 
+// ---------------------------------------------------------------------------
+// packed block-scaled FP8 rows (584 bytes)
+// ---------------------------------------------------------------------------
+//
+// FlashInfer "trtllm_batch_decode_sparse_mla_dsv4" (introduction,
+// packed-backend paragraph; parameter swa_kv_cache) gives the row's size,
+// 584 bytes of uint8 per token, and vLLM DeepseekV4FlashInferMLAAttention
+// (class comment on use_flashmla_fp8_layout) its family, UE8M0 block-scaled
+// FP8.  The byte order is read as: NoPE dims 0..447 as E4M3FN codes (bytes
+// 0..447), RoPE dims 448..511 as little-endian BF16 (bytes 448..575), then
+// one UE8M0 scale byte per 56 NoPE dims (bytes 576..583); NoPE dim d is
+// E4M3FN(byte d) * 2^(scale[d / 56] - 127).
+//
+// In the kernels a packed row reaches its BF16 LDS tile row in two parts:
+//  * lanes 0..55 load the 8 NoPE codes of dims [8 lane, 8 lane + 8) through
+//    registers, exactly as per-tensor FP8 rows do, and widen them with their
+//    block's scale when the tile is written (E4M3FN times a power of two is
+//    exactly a BF16 value in the normal range);
+//  * the RoPE dims (already BF16) and the scale bytes go by one 9-lane
+//    LDS-DMA straight into the tile row: lane j < 8 moves bytes
+//    [448 + 16 j, +16) to row offset 896 + 16 j, lane 8 moves bytes
+//    [568, 584) (the last RoPE dims again, then the 8 scale bytes) to the
+//    row's padding at offset 1024, so the scale bytes sit at 1032..1039.
+constexpr int kPackedRowBytes = 584;
+constexpr int kPackedNopeLanes = 56;       // lanes holding 8 NoPE codes each
+constexpr int kPackedBlockLanes = 7;       // 56 dims per scale = 7 lanes
+constexpr int kPackedScaleLds = 1032;      // scale bytes in the LDS row
+static_assert(kPackedScaleLds + 8 <= kRowPitch, "scale bytes fit the row padding");
+
+// The RoPE dims and scale bytes of one packed row into its LDS tile row
+// (lds_row = the row's LDS byte address).  Only lanes 0..8 take part: the
+// exec mask is narrowed and restored inside the statement, so the compiler
+// sees one straight-line instruction group.  `tail_off` is the lane's byte
+// offset in the row (448 + 16 lane for lanes 0..7, 568 for lane 8).  The
+// buffer resource covers exactly the row.
+__device__ __forceinline__ void packed_tail_dma(const uint8_t* row, uint32_t tail_off,
+                                                uint32_t lds_row) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)row, (short)0, kPackedRowBytes, kRawBufferWord3);
+  uint64_t saved_exec;
+  uint32_t saved_m0;
+  // s_nop 4: the row address may come from a VALU write of an SGPR
+  // (v_readlane); s_nop 1 after the EXEC write and s_nop 0 after the M0
+  // write before the LDS-DMA.
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b64 %0, exec\n\t"
+      "s_mov_b64 exec, 0x1ff\n\t"
+      "s_mov_b32 %1, m0\n\t"
+      "s_mov_b32 m0, %4\n\t"
+      "s_nop 1\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_mov_b64 exec, %0"
+      : "=&s"(saved_exec), "=&s"(saved_m0)
+      : "v"(tail_off), "s"(rs), "s"(lds_row + 896u)
+      : "memory");
+}
+
+// UE8M0 scale byte -> the binary32 power of two 2^(e - 127) (e = 255: NaN).
+__device__ __forceinline__ float ue8m0_scale(uint32_t e) {
+  const uint32_t bits = e == 0u ? 0x00400000u : (e == 255u ? 0x7FC00000u : e << 23);
+  return __uint_as_float(bits);
+}
+
+// 8 E4M3FN codes times a power-of-two scale -> 8 BF16 values (exact for
+// results in BF16's normal range).
+__device__ __forceinline__ u32x4 widen_e4m3fn_x8_scaled(u32x2 v, float scale) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[0], scale, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], scale, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v[1], scale, true));
+  return r;
+}
+
+// The lane's NoPE codes (registers) of a packed row into its LDS tile row,
+// widened with the scale byte the row's DMA put in the padding.  The scale
+// read takes its address through `codes`, so it cannot be scheduled before
+// the codes (and, the DMA having been issued first, the scale bytes) have
+// landed.  Lanes 56..63 hold RoPE bytes the DMA already placed: no store.
+__device__ __forceinline__ void packed_store_row(uint8_t* lds_row, int lane, u32x2 codes) {
+  uint32_t dep = codes[0];
+  asm volatile("v_and_b32 %0, 0, %0" : "+v"(dep));
+  if (lane < kPackedNopeLanes) {
+    const uint32_t e = lds_row[kPackedScaleLds + lane / kPackedBlockLanes + dep];
+    *(u32x4*)(lds_row + lane * 16) = widen_e4m3fn_x8_scaled(codes, ue8m0_scale(e));
+  }
+}
+
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
                                              int c) {
   if (atomicCAS(err, 0, code) == 0) {
@@ -363,9 +453,10 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
   return 8 * (i >> 2) + 4 * kg + (i & 3);
 }
 
-template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN>
+template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false>
 __global__ __launch_bounds__(NW * 64, 1)
 void decode_kernel(DecodeParams p) {
+  static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
   constexpr int H = NW * 32;              // one wave per 32 heads
   constexpr int NT = NW * 64;
   constexpr int RPW = kTile / NW;         // tile rows each wave gathers
@@ -667,6 +758,9 @@ void decode_kernel(DecodeParams p) {
       typedef u32x2 stage_t;
       const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
       const uint32_t lane_off = (uint32_t)lane * (VW * 4);
+      // packed rows: the lane's byte offset of the RoPE / scale DMA
+      const uint32_t tail_off = lane < 8 ? 448u + 16u * (uint32_t)lane : 568u;
+      const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
       stage_t st[RPW];
       auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
         const int s0 = tile * kTile + wave_u * RPW;
@@ -683,16 +777,24 @@ void decode_kernel(DecodeParams p) {
         code = (s0 + jj < n_act) ? code : last_code;
         const uint8_t* base = code < 0 ? p.comp : p.swa;
         const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+        if constexpr (PACKED)
+          packed_tail_dma(row, tail_off,
+                          lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes +
+                                                (wave_u * RPW + jj) * kRowPitch));
         st[jj] = load_row8(row, lane_off);
       };
       auto store = [&](int tile) {
         uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
 #pragma unroll
         for (int jj = 0; jj < RPW; ++jj) {
-          u32x4 v;
-          if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
-          else v = st[jj];
-          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
+          if constexpr (PACKED) {
+            packed_store_row(dst + (wave_u * RPW + jj) * kRowPitch, lane, st[jj]);
+          } else {
+            u32x4 v;
+            if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
+            else v = st[jj];
+            *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
+          }
         }
       };
       // prologue: tiles 0 .. NSTAGE-2 into their stages
@@ -810,8 +912,9 @@ struct BoolC {
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false,
-          bool STREAM = false>
+          bool STREAM = false, bool PACKED = false>
 __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
+  static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
   constexpr int NW = 4, H = 128, NT = 256;
   constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
   // LDS tiles: i-1 (read by O^T), i (S^T), i+1 and i+2 (landing).
@@ -1175,21 +1278,37 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         u32x2 rs0[RPW], rs1[RPW];
         const uint8_t* rows[RPW];
         const uint32_t lane_off8 = (uint32_t)lane * 8u;
-        auto load_set = [&](u32x2 (&rs)[RPW]) {
+        // packed rows: the lane's byte offset of the RoPE / scale DMA
+        const uint32_t tail_off = lane < 8 ? 448u + 16u * (uint32_t)lane : 568u;
+        // LDS byte address of the wave's row jj of `tile`
+        auto lds_row_addr = [&](int tile, int jj) -> uint32_t {
+          return lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
+                 (uint32_t)((wave_u * RPW + jj) * kRowPitch);
+        };
+        // one row of `tile` into a register set (a packed row's RoPE dims
+        // and scale bytes first go straight to LDS)
+        auto load_one = [&](int tile, int jj, u32x2& r) {
+          if constexpr (PACKED) packed_tail_dma(rows[jj], tail_off, lds_row_addr(tile, jj));
+          r = load_row8(rows[jj], lane_off8);
+        };
+        auto load_set = [&](int tile, u32x2 (&rs)[RPW]) {
 #pragma unroll
-          for (int jj = 0; jj < RPW; ++jj) rs[jj] = load_row8(rows[jj], lane_off8);
+          for (int jj = 0; jj < RPW; ++jj) load_one(tile, jj, rs[jj]);
         };
         auto store_set = [&](int tile, const u32x2 (&rs)[RPW]) {
-          uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes + wave_u * RPW * kRowPitch +
-                         lane * 16;
+          uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes + wave_u * RPW * kRowPitch;
 #pragma unroll
-          for (int jj = 0; jj < RPW; ++jj)
-            *(u32x4*)(dst + jj * kRowPitch) = widen_e4m3fn_x8(rs[jj]);
+          for (int jj = 0; jj < RPW; ++jj) {
+            if constexpr (PACKED)
+              packed_store_row(dst + jj * kRowPitch, lane, rs[jj]);
+            else
+              *(u32x4*)(dst + jj * kRowPitch + lane * 16) = widen_e4m3fn_x8(rs[jj]);
+          }
         };
         fetch_rows(0, rows);
-        load_set(rs0);
+        load_set(0, rs0);
         fetch_rows(1, rows);
-        load_set(rs1);
+        load_set(1, rs1);
         fetch_rows(min(2, ntiles - 1), rows);
         store_set(0, rs0);
         // One iteration; PAR = it & 1 names the register set of tile it+2.
@@ -1214,8 +1333,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           f32x16 sv;
           if constexpr (kQK) {
             sv = qk(stage(it), [&](int kk) {
-              if (kLoad && (kk & 3) == 3)
-                rs_next[kk >> 2] = load_row8(rows[kk >> 2], lane_off8);
+              if (kLoad && (kk & 3) == 3) load_one(it + 2, kk >> 2, rs_next[kk >> 2]);
             });
             mfma_qk_drain(sv);
             mask_tail(sv, it);
@@ -1330,6 +1448,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
   } while (again);
   if constexpr (GATHER_ONLY) return;
+  // Packed rows: the last iterations may have issued RoPE / scale DMAs for
+  // clamped (re-read) rows of no tile; they must land before the epilogue
+  // reuses the tile memory.
+  if constexpr (PACKED) wait_vmcnt<0>();
 
   // ---- epilogue: the head owner finishes its head's normaliser ------------
   {
@@ -1398,10 +1520,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 }
 
-template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM, bool PACKED = false>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
-  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN, STREAM>(p);
+  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN, STREAM, PACKED>(p);
 }
 
 // The row gather of decode_hd_kernel alone (BF16 rows), under its own name.
@@ -1595,19 +1717,34 @@ hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
   return launch_decode_hd_s<QF, KF, false>(p, stream);
 }
 
-template <int NW, bool QF, bool KF>
+// Packed block-scaled FP8 rows (BF16 q), H = 128.
+hipError_t launch_decode_hd_packed(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.T * p.S));
+  const bool gen = p.segmented != 0;
+  if (p.S > 1 && gen)
+    hipLaunchKernelGGL((decode_hd_kernel<false, true, true, true, false, true>), grid, dim3(256), 0, stream, p);
+  else if (p.S > 1)
+    hipLaunchKernelGGL((decode_hd_kernel<false, true, true, false, false, true>), grid, dim3(256), 0, stream, p);
+  else if (gen)
+    hipLaunchKernelGGL((decode_hd_kernel<false, true, false, true, false, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_hd_kernel<false, true, false, false, false, true>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int NW, bool QF, bool KF, bool PK = false>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const dim3 block(NW * 64);
   const bool gen = p.segmented != 0;
   if (p.S > 1 && gen)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, true, PK>), grid, block, 0, stream, p);
   else if (p.S > 1)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false, PK>), grid, block, 0, stream, p);
   else if (gen)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, true, PK>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false, PK>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1651,6 +1788,11 @@ hipError_t noalloc_scratch(void** out) {
 
 hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream) {
+  if (kv_dtype == kKvPacked584) {        // BF16 q only (checked on the host)
+    if (q_dtype != 0) return hipErrorInvalidValue;
+    if (p.H == 64) return launch_decode_t<2, false, true, true>(p, stream);
+    return launch_decode_hd_packed(p, stream);
+  }
   const bool qf = q_dtype != 0, kf = kv_dtype != 0;
   if (p.H == 64) {
     if (!qf && !kf) return launch_decode_t<2, false, false>(p, stream);

@@ -27,6 +27,8 @@ STATUS = {
 NOALLOC_SCRATCH_BYTES = 64 << 20
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3FN = 1
+DTYPE_PACKED_FP8_584 = 2        # uint8 pools of 584-byte packed rows
+PACKED_ROW_BYTES = 584
 FLAG_VALIDATE_INDICES = 1
 DEVERR = {0: "none", 1: "index out of range", 2: "topk_len out of range"}
 
@@ -197,6 +199,8 @@ def dtype_code(t: torch.Tensor) -> int:
         return DTYPE_BF16
     if t.dtype == torch.float8_e4m3fn:
         return DTYPE_FP8_E4M3FN
+    if t.dtype == torch.uint8 and t.dim() == 2 and t.shape[1] == PACKED_ROW_BYTES:
+        return DTYPE_PACKED_FP8_584
     raise TypeError(f"unsupported element type {t.dtype}")
 
 
@@ -224,8 +228,10 @@ def _check_tensors(q, out, out_lse, pools, tables, vectors, sinks):
                  and out_lse.is_contiguous(), "out_lse must be a contiguous fp32 [T, H]")
     live = [p for p in pools if p is not None]
     for p in live:
-        _require(p.dim() == 2 and p.shape[1] == 512 and p.stride(1) == 1,
-                 "pools must be [rows, 512] with unit column stride")
+        width = PACKED_ROW_BYTES if p.dtype == torch.uint8 else 512
+        _require(p.dim() == 2 and p.shape[1] == width and p.stride(1) == 1,
+                 "pools must be [rows, 512] (uint8 packed rows: [rows, 584]) "
+                 "with unit column stride")
     if len(live) == 2:
         _require(live[0].dtype == live[1].dtype, "both pools must have one dtype")
         _require(live[0].stride(0) == live[1].stride(0),

@@ -130,13 +130,15 @@ def normal_rows(rows: int, seed: int, device="cpu", dtype: str = BF16,
 
 
 def packed_rows(rows: int, seed: int, device="cpu", chunk_rows: int = 1 << 17,
-                spread: int = 8) -> torch.Tensor:
+                spread: int = 1) -> torch.Tensor:
     """[rows, 584] uint8 packed block-scaled FP8 rows, written the way a KV
     cache writer would fill them (the layout the library and the oracle read:
     bytes 0..447 E4M3FN NoPE codes, 448..575 the 64 RoPE dims as BF16,
     576..583 one UE8M0 scale byte per 56 NoPE dims).  Values are N(0,1),
     each 56-dim NoPE block multiplied by a seeded 2^k, k uniform in
-    [-spread, spread], so the scale bytes vary; a block's scale is the
+    [-spread, spread] (default 1: magnitudes stay those of N(0,1) latents
+    within a factor 2, the scale bytes vary from block to block); a block's
+    scale is the
     smallest power of two 2^(e-127) with max|x| / 2^(e-127) <= 448, and its
     codes are torch's float8_e4m3fn cast of x / 2^(e-127)."""
     device = torch.device(device)

@@ -143,7 +143,7 @@ def call(so, a, p=None, T=None):
     ("T", -1, 1), ("K", 0, 1), ("H", 96, 3), ("H", 256, 3),
     ("q", None, 1), ("swa_pool", None, 1), ("indices", None, 1),
     ("out", None, 1), ("compressed_pool", None, 1),
-    ("swa_rows", -5, 1), ("q_dtype", 1, 2), ("kv_dtype", 2, 2),
+    ("swa_rows", -5, 1), ("q_dtype", 1, 2), ("kv_dtype", 3, 2),
     ("q", DUMMY + 8, 5), ("out", DUMMY + 2, 5), ("swa_pool", DUMMY + 4, 5),
     ("compressed_pool", DUMMY + 8, 5), ("indices", DUMMY + 2, 5),
     ("pool_row_stride", 500, 1), ("pool_row_stride", 516, 5),
@@ -209,6 +209,32 @@ def test_noalloc_host_checks(so):
     a.bmm1_scale = 0.0
     assert so.sparse_mla_decode_noalloc(ctypes.byref(a), ctypes.byref(plan(4, 128, 256)),
                                         None) == 1
+
+
+def test_packed_rows_argument_checks(so):
+    """Packed 584-byte rows: only with BF16 q; the row stride is in bytes,
+    0 meaning 584, at least 584 and a multiple of 8.  Calls that pass the
+    checks are stopped at a forced plan mismatch (nothing is launched)."""
+    pk = L.DTYPE_PACKED_FP8_584
+    a = good_args()
+    a.kv_dtype = pk
+    p = plan(4, 128, 256, kv=pk)
+    p.K = 999
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 6
+    for stride, code in ((584, 6), (592, 6), (583, 1), (512, 1), (588, 5)):
+        a.pool_row_stride = stride
+        assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == code, stride
+    a.pool_row_stride = 0
+    a.q_dtype = L.DTYPE_FP8_E4M3FN
+    assert so.sparse_mla_decode(ctypes.byref(a), ctypes.byref(p), None) == 2
+    # the planner takes the pair too, and rejects FP8 q with packed rows
+    assert L.plan_splits(512, 128, 2048, 0, pk, num_cus=256).num_splits >= 1
+    q = L.Plan()
+    assert so.sparse_mla_plan_splits(4, 128, 256, 1, pk, 0, 0, 256, ctypes.byref(q)) == 2
+    # gather_only serves BF16 rows only
+    a = good_args()
+    a.kv_dtype = pk
+    assert call_gather(so, a) == 2
 
 
 def test_decode_null_args_and_empty_batch(so):

@@ -177,6 +177,24 @@ def test_packed_decode_matches_the_multiset_brute_force():
     assert np.allclose(ref["lse"], bf_lse, rtol=0, atol=1e-12)
 
 
+def test_empty_token_with_packed_rows():
+    """A token with no active slot gives out = 0 and lse = the sink's own
+    term (or -inf without a sink), with packed pools as with any other."""
+    swa = W.packed_rows(8, seed=31).numpy()
+    q = np.zeros((2, 3, 512), np.uint16)
+    idx = np.full((2, 130), -1, np.int32)
+    idx[1, 2] = 5
+    sinks = np.array([0.5, -1.0, 2.0], np.float32)
+    for sk in (sinks, None):
+        ref = oracle.sparse_mla_decode(q, "bf16", swa, swa, "packed_fp8_584", idx,
+                                       np.array([0, 130], np.int32), sk, 0.1, 1.0, 1.0)
+        assert ref["out"].shape == (2, 3, 512) and not ref["out"][0].any()
+        if sk is None:
+            assert np.all(np.isneginf(ref["lse"][0]))
+        else:
+            assert np.allclose(ref["lse"][0], sinks.astype(np.float64) / math.log(2.0))
+
+
 @pytest.mark.parametrize("mistake", ["block64", "big_endian", "bias128", "scale_first"])
 def test_planted_layout_mistakes_fail(mistake):
     """Plausible misreadings of the layout, planted in a copy of the decode,
