@@ -117,15 +117,19 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libsparsemla.so from the package directory (no fallback)."""
+    """Load libsparsemla.so from the package directory (no fallback).  The
+    environment variable SPARSEMLA_LIB names another build of the same ABI
+    instead (the sanitizer build of the host layer that the host tests run
+    against)."""
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB_PATH):
+    path = os.environ.get("SPARSEMLA_LIB") or LIB_PATH
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{LIB_PATH} is missing; build it first "
+            f"{path} is missing; build it first "
             "(python -m sparse_mla_decode_gather_amd.build)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     lib.sparse_mla_plan_splits.argtypes = [ctypes.c_int] * 8 + [
         ctypes.POINTER(Plan)]
     lib.sparse_mla_plan_splits.restype = ctypes.c_int
