@@ -175,37 +175,32 @@ __device__ __forceinline__ void wait_vmcnt() {
 // STREAM: the load carries the non-temporal hint, for calls whose gathered
 // rows are too many to still be cached when the next call runs (see
 // kStreamingBytes below).
-template <bool STREAM = false>
+template <bool STREAM = false, bool ADDR_SETTLED = false>
 __device__ __forceinline__ void lds_dma_row16(const uint8_t* row,
                                               uint32_t lane_off,
                                               uint32_t lds_addr) {
   uint32_t saved;
   // s_nop 4: the row address may have just been written by a VALU
   // (v_readlane / v_readfirstlane), and a VMEM read of a VALU-written SGPR
-  // needs 5 wait states; s_nop 0: M0 written by SALU before LDS-DMA.
-  if constexpr (STREAM) {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2 nt\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(lane_off), "s"(row), "s"(lds_addr)
-        : "memory");
-  } else {
-    asm volatile(
-        "s_nop 4\n\t"
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(lane_off), "s"(row), "s"(lds_addr)
-        : "memory");
-  }
+  // needs 5 wait states.  ADDR_SETTLED: the caller guarantees that more
+  // than 5 instructions separate that write from this load (the steady
+  // tile loop, whose row addresses are read out one iteration earlier).
+  // s_nop 0: M0 written by SALU before LDS-DMA.
+#define SMLA_DMA_BODY(NOP, NT)                     \
+  asm volatile(NOP                                 \
+               "s_mov_b32 %0, m0\n\t"              \
+               "s_mov_b32 m0, %3\n\t"              \
+               "s_nop 0\n\t"                       \
+               "global_load_lds_dwordx4 %1, %2" NT "\n\t" \
+               "s_mov_b32 m0, %0"                  \
+               : "=&s"(saved)                      \
+               : "v"(lane_off), "s"(row), "s"(lds_addr) \
+               : "memory")
+  if constexpr (STREAM && ADDR_SETTLED) SMLA_DMA_BODY("", " nt");
+  else if constexpr (STREAM) SMLA_DMA_BODY("s_nop 4\n\t", " nt");
+  else if constexpr (ADDR_SETTLED) SMLA_DMA_BODY("", "");
+  else SMLA_DMA_BODY("s_nop 4\n\t", "");
+#undef SMLA_DMA_BODY
 }
 
 // 8 bytes through a global (not flat) pointer (FP8 q: a per-lane head
@@ -1054,10 +1049,13 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   bool need_sticky = false;
 
   constexpr int kLead = KV_FP8 ? 3 : 4;
-  auto qk = [&](const uint8_t* tb, auto&& every) -> f32x16 {
+  // `after_lead` runs once the first kLead operand reads are out (LDS reads
+  // return in order, so reads issued there do not delay the first MFMA).
+  auto qk = [&](const uint8_t* tb, auto&& every, auto&& after_lead) -> f32x16 {
     bf16x8 a[kLead];
 #pragma unroll
     for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
+    after_lead();
     f32x16 acc;
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) {
@@ -1232,20 +1230,27 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     // the code of row j on the VALU, then each address is read out of its
     // lane (a few instructions per tile instead of a scalar multiply chain
     // per row).
-    auto fetch_rows = [&](int tile, const uint8_t* (&rows)[RPW]) {
-      const int code = slots[tile * kTile + wave_u * RPW + (lane & (RPW - 1))];
+    // ... in three steps, so that the steady tile loop can spread them over
+    // its MFMAs: the slot code (an LDS read), the lane's row address, and
+    // the address of row jj read out of lane jj.
+    auto row_code = [&](int tile) -> int {
+      return slots[tile * kTile + wave_u * RPW + (lane & (RPW - 1))];
+    };
+    auto row_addr = [&](int code) -> uint64_t {
       const uint8_t* base = code < 0 ? p.comp : p.swa;
-      const uint64_t a = (uint64_t)(uintptr_t)(
-          base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
-      const int alo = (int)(uint32_t)a, ahi = (int)(uint32_t)(a >> 32);
+      return (uint64_t)(uintptr_t)(base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
+    };
+    auto row_of_lane = [&](uint64_t a, int jj) -> const uint8_t* {
+      // (readlane returns int: widen through uint32_t, not with sign
+      // extension)
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, jj);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), jj);
+      return (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+    };
+    auto fetch_rows = [&](int tile, const uint8_t* (&rows)[RPW]) {
+      const uint64_t a = row_addr(row_code(tile));
 #pragma unroll
-      for (int jj = 0; jj < RPW; ++jj) {
-        // (readlane returns int: widen through uint32_t, not with sign
-        // extension)
-        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane(alo, jj);
-        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane(ahi, jj);
-        rows[jj] = (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
-      }
+      for (int jj = 0; jj < RPW; ++jj) rows[jj] = row_of_lane(a, jj);
     };
     auto mask_tail = [&](f32x16& sv, int it) {
       const int nt = n_in(it);
@@ -1261,6 +1266,11 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
                            (uint32_t)((wave_u * RPW + jj) * kRowPitch);
       lds_dma_row16<STREAM>(row, lane_off, dst);
+    };
+    // The same, from a tile base computed once (the wave's first row of the
+    // tile's stage), with row addresses read out an iteration earlier.
+    auto issue_row_settled = [&](uint32_t tile_base, int jj, const uint8_t* row) {
+      lds_dma_row16<STREAM, true>(row, lane_off, tile_base + (uint32_t)(jj * kRowPitch));
     };
     // The first row gathers go out without waiting for Q: loads retire in
     // order, so the wait for tile 0 also covers Q.  (The compiler's own
@@ -1334,7 +1344,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           if constexpr (kQK) {
             sv = qk(stage(it), [&](int kk) {
               if (kLoad && (kk & 3) == 3) load_one(it + 2, kk >> 2, rs_next[kk >> 2]);
-            });
+            }, [] {});
             mfma_qk_drain(sv);
             mask_tail(sv, it);
           } else {
@@ -1385,7 +1395,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         }
         f32x16 sv = qk(stage(it), [&](int kk) {
           if (do_issue && (kk & 3) == 3) issue_row(it + 2, kk >> 2, rows[kk >> 2]);
-        });
+        }, [] {});
         mfma_qk_drain(sv);
         mask_tail(sv, it);
         return sv;
@@ -1408,25 +1418,62 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           step_block(BoolC<false>{}, kv_lds, p_lds, pfr, vfr, sv0, p_lds, no_hook);
         if (di) fetch_rows(min(3, ntiles - 1), rows);
       }
-      for (int it = 1; it <= ntiles; ++it) {
-        if (it < ntiles) land(it);
-        else __syncthreads();
-        const bool di = it + 2 < ntiles;
+      // Iteration it: land tile it, O^T of tile it-1 with the S^T and
+      // softmax of tile it, the rows of tile it+2 issued during S^T.  STEADY
+      // iterations (it + 2 < ntiles) are a compile-time variant: every row
+      // issue happens and tile it is whole, so the body has no branches.
+      auto iteration = [&](auto steady, int it) {
+        constexpr bool kSteady = decltype(steady)::value && !GATHER_ONLY;
+        if constexpr (kSteady) {
+          wait_vmcnt<RPW>();
+          __syncthreads();
+        } else {
+          if (it < ntiles) land(it);
+          else __syncthreads();
+        }
+        const bool di = kSteady || it + 2 < ntiles;
         const u32x4* pr = p_lds + ((it - 1) & 1) * kPBuf;
         bf16x8 pfr[NHB], vfr[kVLead];
-        if constexpr (!GATHER_ONLY) pv_prefetch(stage(it - 1), pr, pfr, vfr);
         f32x16 sv;
-        if (it < ntiles) {
+        if constexpr (kSteady) {
+          // the first S^T operand reads go out before the O^T operand reads
+          const uint32_t tile_base = lds_base + (uint32_t)(((it + 2) % NSTAGE) * kTileBytes) +
+                                     (uint32_t)(wave_u * RPW * kRowPitch);
+          sv = qk(stage(it), [&](int kk) {
+            if ((kk & 3) == 3) issue_row_settled(tile_base, kk >> 2, rows[kk >> 2]);
+          }, [&] { pv_prefetch(stage(it - 1), pr, pfr, vfr); });
+          mfma_qk_drain(sv);
+        } else if (it < ntiles) {
+          if constexpr (!GATHER_ONLY) pv_prefetch(stage(it - 1), pr, pfr, vfr);
           sv = qk_tile(it, di);
         } else {
+          if constexpr (!GATHER_ONLY) pv_prefetch(stage(it - 1), pr, pfr, vfr);
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
         }
-        if constexpr (!GATHER_ONLY)
+        if constexpr (kSteady) {
+          // The rows of tile it+3 (their addresses are no longer needed for
+          // tile it+2, whose loads went out above): the slot code is read
+          // under the first O^T MFMAs, the readouts into SGPRs go between the
+          // last ones, which have no softmax work beside them.
+          int code = 0;
+          uint64_t addr = 0;
           step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
-                     p_lds + (it & 1) * kPBuf, no_hook);
-        if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
-      }
+                     p_lds + (it & 1) * kPBuf, [&](int k) {
+                       if (k == 4) code = row_code(min(it + 3, ntiles - 1));
+                       if (k == 20) addr = row_addr(code);
+                       if (k >= 21 && k < 21 + RPW) rows[k - 21] = row_of_lane(addr, k - 21);
+                     });
+        } else {
+          if constexpr (!GATHER_ONLY)
+            step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
+                       p_lds + (it & 1) * kPBuf, no_hook);
+          if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
+        }
+      };
+      int it = 1;
+      for (; it + 2 < ntiles; ++it) iteration(BoolC<true>{}, it);
+      for (; it <= ntiles; ++it) iteration(BoolC<false>{}, it);
     }
     if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
     __syncthreads();
