@@ -1078,7 +1078,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   // instance of this block updates O, so O keeps one register assignment.
   // O^T operands from LDS: V^T fragment f = 4h + db (rows 16h.., dims
   // block db of this wave) and P^T fragment (h, hb).
-  constexpr int kVLead = 2;
+  constexpr int kVLead = KV_FP8 ? 3 : 4;
   auto vfrag = [&](const uint8_t* vt, int f) -> bf16x8 {
     const uint8_t* vb = vt + tr_off + (16 * (f >> 2)) * kRowPitch + (f & 3) * 64;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1355,9 +1355,19 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           // register sets leave no room to hold them across S^T)
           bf16x8 pfr[NHB], vfr[kVLead];
           if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
-          step_block(pv, vt, pr, pfr, vfr, sv, p_lds + (it & 1) * kPBuf, no_hook);
+          // the row addresses of tile it+3 (those of tile it+2 were used by
+          // the loads above): slot code under the first MFMAs, readouts
+          // between the last ones, which have no softmax work beside them
+          int code = 0;
+          uint64_t addr = 0;
+          step_block(pv, vt, pr, pfr, vfr, sv, p_lds + (it & 1) * kPBuf, [&](int k) {
+            if constexpr (kLoad) {
+              if (k == 4) code = row_code(min(it + 3, ntiles - 1));
+              if (k == 20) addr = row_addr(code);
+              if (k >= 21 && k < 21 + RPW) rows[k - 21] = row_of_lane(addr, k - 21);
+            }
+          });
           if constexpr (kStore) store_set(it + 1, rs_land);
-          if constexpr (kLoad) fetch_rows(min(it + 3, ntiles - 1), rows);
         };
         using T_ = BoolC<true>;
         using F_ = BoolC<false>;
