@@ -74,6 +74,12 @@ typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// A compile-time bool as a value (selects variants of generic lambdas).
+template <bool B>
+struct BoolC {
+  static constexpr bool value = B;
+};
+
 // ---------------------------------------------------------------------------
 // element conversions
 // ---------------------------------------------------------------------------
@@ -570,7 +576,8 @@ void decode_kernel(DecodeParams p) {
   // Online softmax of one tile's S^T; returns P^T as the two B operands of
   // the PV steps.  Rows past n_tile (a ragged last tile) repeat the tile's
   // last active row: they cannot raise the max and get probability 0.
-  auto softmax = [&](f32x16 sv, int n_tile, bf16x8 (&pf)[2]) {
+  auto softmax = [&](f32x16 sv, int n_tile, bf16x8 (&pf)[2], auto full) {
+    constexpr bool kFull = decltype(full)::value;   // n_tile == kTile known
     mfma_qk_drain(sv);
     float smax = sv[0];
 #pragma unroll
@@ -593,7 +600,7 @@ void decode_kernel(DecodeParams p) {
         const int i0 = 8 * h + 2 * k;
         float p0 = fast_exp2(__builtin_fmaf(sv[i0], p.scale_log2, neg_m));
         float p1 = fast_exp2(__builtin_fmaf(sv[i0 + 1], p.scale_log2, neg_m));
-        if (n_tile < kTile) {         // wave-uniform; only a ragged last tile
+        if (!kFull && n_tile < kTile) {   // wave-uniform; only a ragged last tile
           p0 = (tile_row_of_reg(i0, kg) < n_tile) ? p0 : 0.f;
           p1 = (tile_row_of_reg(i0 + 1, kg) < n_tile) ? p1 : 0.f;
         }
@@ -724,13 +731,16 @@ void decode_kernel(DecodeParams p) {
       };
       const int pro = min(NSTAGE - 1, ntiles);
       for (int tl = 0; tl < pro; ++tl) issue(tl);
-      for (int it = 0; it < ntiles; ++it) {
+      // STEADY iterations (the rows of a later tile go out, tile it is
+      // whole) are a compile-time variant with no branches in their body.
+      auto iteration = [&](auto steady, int it) {
+        constexpr bool kSteady = decltype(steady)::value;
         wait_tile(it, min(it + NSTAGE - 2, ntiles - 1));
         __syncthreads();            // every wave's rows landed; tile it-1 done
         // The rows of tile it+NSTAGE-1 go out while the S^T MFMAs of tile
         // it run (RPW rows, spread over the 32 MFMAs).
         const int nxt = it + NSTAGE - 1;
-        const bool do_issue = nxt < ntiles;
+        const bool do_issue = kSteady || nxt < ntiles;
         int codes[RPW];
         fetch_codes(do_issue ? nxt : it, codes);
         const f32x16 sv = qk(stage(it), [&](int q) {
@@ -740,9 +750,12 @@ void decode_kernel(DecodeParams p) {
             if (do_issue) issue_row(nxt, q * (RPW / 8) + r, codes);
         });
         bf16x8 pf[2];
-        softmax(sv, n_in(it), pf);
+        softmax(sv, n_in(it), pf, steady);
         pv(stage(it), pf);
-      }
+      };
+      int it = 0;
+      for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
+      for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
     } else {
       // Register-staged gather of FP8 rows: lane `lane` carries 8 B of a row,
       // widened to BF16 when written to LDS.  The loads of tile it+NSTAGE-1
@@ -800,10 +813,13 @@ void decode_kernel(DecodeParams p) {
         for (int jj = 0; jj < RPW; ++jj) load_row(tl, jj, codes);
         store(tl);
       }
-      for (int it = 0; it < ntiles; ++it) {
+      // STEADY iterations (the next tile is loaded, tile it is whole) are a
+      // compile-time variant with no branches in their body.
+      auto iteration = [&](auto steady, int it) {
+        constexpr bool kSteady = decltype(steady)::value;
         __syncthreads();            // tile it stored by every wave; it-1 done
         const int nxt = it + NSTAGE - 1;
-        const bool do_load = nxt < ntiles;
+        const bool do_load = kSteady || nxt < ntiles;
         int codes[RPW];
         fetch_codes(do_load ? nxt : it, codes);
         const f32x16 sv = qk(stage(it), [&](int q) {
@@ -812,10 +828,13 @@ void decode_kernel(DecodeParams p) {
             if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
         });
         bf16x8 pf[2];
-        softmax(sv, n_in(it), pf);
+        softmax(sv, n_in(it), pf, steady);
         pv(stage(it), pf);
         if (do_load) store(nxt);
-      }
+      };
+      int it = 0;
+      for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
+      for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
     }
     // did any wave's tile outgrow its reference max?
     if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
@@ -895,11 +914,6 @@ void decode_kernel(DecodeParams p) {
 // list is padded to whole tiles, a tile's row addresses are computed by
 // one VALU pass (one row per lane) and read out into SGPRs, and each row
 // costs one load instruction.
-
-template <bool B>
-struct BoolC {
-  static constexpr bool value = B;
-};
 
 // KV_FP8: E4M3FN rows go through registers (two tiles ahead, in two
 // register sets) and are widened to BF16 as they are written to LDS; BF16
