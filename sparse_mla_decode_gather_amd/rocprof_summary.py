@@ -2,7 +2,7 @@
 
     python -m sparse_mla_decode_gather_amd.rocprof_summary stats <dir> <cmd>
     python -m sparse_mla_decode_gather_amd.rocprof_summary traffic \\
-        <fetch_dir> <write_dir> <copy_bytes> <cmd>
+        <fetch_dir> <write_dir> <copy_bytes> <cmd> [<request_dir>]
     python -m sparse_mla_decode_gather_amd.rocprof_summary sq <cmd> <dir>...
 
 ``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv): the
@@ -15,7 +15,9 @@ into HBM bytes per decode launch, calibrated by the same counters on a
 plain device copy of known size taken in the same process: the factor is
 counter bytes / true bytes of the copy, and decode traffic = counter
 bytes / factor.  The result is tagged with a digest of the kernel sources,
-so a stale figure is ignored once the kernel changes.
+so a stale figure is ignored once the kernel changes.  With a third run of
+the EA read-request counters by size (TCC_EA0_RDREQ_sum, _128B_sum,
+_32B_sum) the summary adds an uncalibrated cross-check of the read bytes.
 """
 
 from __future__ import annotations
@@ -73,7 +75,19 @@ def _per_dispatch(rows, counter, pattern_ok):
     return list(per.values())
 
 
-def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cmd: str) -> str:
+def _req_bytes(rows, pattern_ok):
+    """Read bytes per dispatch from the EA read-request counters: 128-byte,
+    32-byte and (the rest) 64-byte requests."""
+    tot = _per_dispatch(rows, "TCC_EA0_RDREQ_sum", pattern_ok)
+    r128 = _per_dispatch(rows, "TCC_EA0_RDREQ_128B_sum", pattern_ok)
+    r32 = _per_dispatch(rows, "TCC_EA0_RDREQ_32B_sum", pattern_ok)
+    n = min(len(tot), len(r128), len(r32))
+    return [128 * r128[i] + 32 * r32[i] + 64 * (tot[i] - r128[i] - r32[i])
+            for i in range(n)], tot, r128, r32
+
+
+def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cmd: str,
+            req_dir: str = None) -> str:
     is_decode = lambda n: any(d in n for d in DECODE)
     is_copy = lambda n: any(p in n for p in COPY_PATTERNS) and not is_decode(n)
     f_rows = _csv(fetch_dir, "counter_collection.csv")
@@ -106,7 +120,30 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cmd: str) -> str:
         f"write_bytes_per_launch: {write:.0f}",
         f"traffic_bytes_per_launch: {fetch + write:.0f}",
         f"kernel_source_digest: {kernel_source_digest()}",
-    ]) + "\n"
+    ] + ([] if req_dir is None else _req_check(req_dir, is_decode, is_copy, copy_bytes,
+                                               fetch))) + "\n"
+
+
+def _req_check(req_dir, is_decode, is_copy, copy_bytes, fetch):
+    """Cross-check of the calibrated FETCH_SIZE with a second counter set:
+    the EA read requests by size (TCC_EA0_RDREQ_sum, _128B_sum, _32B_sum),
+    uncalibrated, on the decode and on the same plain copy."""
+    rows = _csv(req_dir, "counter_collection.csv")
+    dec, tot, r128, r32 = _req_bytes(rows, is_decode)
+    cpy, _, _, _ = _req_bytes(rows, is_copy)
+    cpy = sorted(cpy)[-3:]
+    d = statistics.median(dec)
+    c = statistics.median(cpy)
+    return [
+        "# cross-check: read bytes from EA read requests by size",
+        "# (128 x RDREQ_128B + 32 x RDREQ_32B + 64 x the other RDREQ), no calibration",
+        f"decode_rdreq_median: {statistics.median(tot):.0f}",
+        f"decode_rdreq_128b_median: {statistics.median(r128):.0f}",
+        f"decode_rdreq_32b_median: {statistics.median(r32):.0f}",
+        f"decode_request_read_bytes: {d:.0f}",
+        f"copy_request_read_bytes_over_true_bytes: {c / copy_bytes:.4f}",
+        f"decode_request_bytes_over_calibrated_fetch: {d / fetch:.4f}",
+    ]
 
 
 def sq(dirs, cmd: str, simds: int = 1024, xcds: int = 8) -> str:
@@ -137,8 +174,8 @@ if __name__ == "__main__":
     if mode == "stats":
         print(stats(sys.argv[2], sys.argv[3]), end="")
     elif mode == "traffic":
-        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5]),
-              end="")
+        print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5],
+                      sys.argv[6] if len(sys.argv) > 6 else None), end="")
     elif mode == "sq":
         print(sq(sys.argv[3:], sys.argv[2]), end="")
     else:
