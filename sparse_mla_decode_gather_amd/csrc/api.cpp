@@ -314,6 +314,12 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   p->S = S;
   p->split_cols = plan->chunks_per_split * plan->chunk_cols;
   p->validate = validate ? 1 : 0;
+  // Longest-first starts only pay when some CU runs more than one item (one
+  // H=128 workgroup fits a CU); without a device count, keep them.
+  {
+    int cus = 0;
+    p->rank_items = (query_cu_count(&cus) != SMLA_OK || (int64_t)a->T * S > cus) ? 1 : 0;
+  }
   if (with_outputs && S > 1) {
     p->mid_lse = reinterpret_cast<float*>(ws + L->mid_lse);
     p->mid_out = reinterpret_cast<uint16_t*>(ws + L->mid_out);

@@ -55,6 +55,9 @@ struct DecodeParams {
   int32_t K2;                    // columns of the second table (slots when paged)
   int32_t segmented;
   int32_t page_size;             // > 0 only when segmented == 2
+  // H=128 kernel: start the items of an XCD longest first (set when the
+  // grid has more items than the device has compute units)
+  int32_t rank_items;
 };
 
 struct CombineParams {

@@ -950,8 +950,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 
   // XCD-aware work mapping (see decode_kernel): XCD x owns the contiguous
   // item range [lo, lo + cnt) and starts its workgroups in the order of
-  // blockIdx.x >> 3.  With per-token lengths, the items of the range are
-  // started longest first (rank by active columns of the item's split, ties
+  // blockIdx.x >> 3.  With per-token lengths, and more items than CUs (the
+  // host sets rank_items; with one item per CU the order cannot matter and
+  // the ranking would only put a dependent load in front of every item's
+  // own loads), the items of the range are started longest first (rank by active columns of the item's split, ties
   // by position): with one or two items per CU, taking them in token order
   // lets the CUs that draw two long tokens set the end of a ragged batch
   // (~9% at 512 tokens of topk_len uniform in [1024, 2048]); longest-first
@@ -966,7 +968,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     const int cnt = q8 + (xcd < r8 ? 1 : 0);
     const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
                             : p.topk_lens != nullptr;
-    if (ragged && cnt > 1 && cnt <= NT) {
+    if (p.rank_items && ragged && cnt > 1 && cnt <= NT) {
       const int tid = threadIdx.x;
       int my_len = -1;
       if (tid < cnt) {
