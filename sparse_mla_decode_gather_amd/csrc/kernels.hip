@@ -1512,12 +1512,18 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     if (threadIdx.x == 0) restart_flag = 0;
     need_sticky = false;
     l_run = 0.f;
+    // A zero made here (opaque to the compiler): a plain 0.f would be
+    // merged with the initial clearing of O, and the compiler would then
+    // keep a block of zero registers alive across the whole tile loop
+    // (spilled to scratch by every workgroup).
+    float zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+        for (int i = 0; i < 16; ++i) o[db][hb][i] = zero;
   }
   } while (again);
   if constexpr (GATHER_ONLY) return;
