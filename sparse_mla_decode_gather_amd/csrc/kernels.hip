@@ -1120,19 +1120,28 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
                         bf16x8 (&pfr)[NHB], bf16x8 (&vfr)[kVLead],
                         f32x16 sv, u32x4* pw, auto&& every) {
     constexpr bool kPV = decltype(do_pv)::value;
-    // P^T operands of the current 16-row half: P^T(1, hb) replaces
-    // P^T(0, hb) right after its last use, four MFMAs before it is needed.
+    // P^T operands of the second 16-row half: with a register set of their
+    // own (kP1Early, BF16 rows) they are read twelve MFMAs ahead of their
+    // first use; otherwise P^T(1, hb) replaces P^T(0, hb) right after its
+    // last use, four MFMAs before it is needed.
+    constexpr bool kP1Early = !KV_FP8;
     float smax = 0.f, neg_m = 0.f, lsum = 0.f, pprev = 0.f;
     u32x4 pk[2];
+    bf16x8 pfr1[NHB];
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (kPV) {
         const int f = k >> 2, hb = k & 3;
+        const bf16x8 pb = (kP1Early && f >= 4) ? pfr1[hb] : pfr[hb];
         o[f & 3][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            vfr[f % kVLead], pfr[hb], o[f & 3][hb], 0, 0, 0);
+            vfr[f % kVLead], pb, o[f & 3][hb], 0, 0, 0);
         if (hb == 3 && f + kVLead < 8) vfr[f % kVLead] = vfrag(vt, f + kVLead);
-        if (f == 3) pfr[hb] = pfrag(pr, 1, hb);
+        if constexpr (kP1Early) {
+          if (f == 2) pfr1[hb] = pfrag(pr, 1, hb);
+        } else {
+          if (f == 3) pfr[hb] = pfrag(pr, 1, hb);
+        }
       }
       if (k == 0) {
         smax = sv[0];
@@ -1229,11 +1238,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         slots[pos++] = last;
       }
     }
-    // The owner of the last active slot pads the tail of the last tile and,
-    // for FP8 rows, one more tile when the count is odd (its rows are all
-    // masked; an even count lets the two register sets alternate statically).
-    const int ntiles = KV_FP8 ? ((n_act + 2 * kTile - 1) / (2 * kTile)) * 2
-                              : (n_act + kTile - 1) / kTile;
+    // The owner of the last active slot pads the tail of the last tile.
+    const int ntiles = (n_act + kTile - 1) / kTile;
     if (cnt > 0 && pos == n_act) {
       for (int i = n_act; i < ntiles * kTile; ++i) slots[i] = last;
     }
@@ -1296,12 +1302,13 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 
     if constexpr (KV_FP8) {
       if (ntiles > 0) {
-        // FP8 rows: each lane loads 8 bytes of each of the wave's 8 rows of
-        // tile it+2 during the S^T MFMAs of tile it, into the register set
-        // of that tile's parity; at the end of iteration it the rows of
-        // tile it+1 are widened and written to LDS.  These are ordinary
-        // loads, so the compiler's own waits are exact.
-        u32x2 rs0[RPW], rs1[RPW];
+        // FP8 rows: each lane loads 8 bytes of each of the wave's 8 rows.
+        // One register set: inside the S^T MFMAs of tile it, row jj of tile
+        // it+1 is widened from it and written to LDS, and then row jj of
+        // tile it+2 is loaded into it, so every load has about one tile of
+        // MFMA work to land.  These are ordinary loads, so the compiler's
+        // own waits are exact.
+        u32x2 rs[RPW];
         const uint8_t* rows[RPW];
         const uint32_t lane_off8 = (uint32_t)lane * 8u;
         // packed rows: the lane's byte offset of the RoPE / scale DMA
@@ -1311,46 +1318,38 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           return lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
                  (uint32_t)((wave_u * RPW + jj) * kRowPitch);
         };
-        // one row of `tile` into a register set (a packed row's RoPE dims
-        // and scale bytes first go straight to LDS)
-        auto load_one = [&](int tile, int jj, u32x2& r) {
+        // one row of `tile` into its register (a packed row's RoPE dims and
+        // scale bytes first go straight to LDS)
+        auto load_one = [&](int tile, int jj) {
           if constexpr (PACKED) packed_tail_dma(rows[jj], tail_off, lds_row_addr(tile, jj));
-          r = load_row8(rows[jj], lane_off8);
+          rs[jj] = load_row8(rows[jj], lane_off8);
         };
-        auto load_set = [&](int tile, u32x2 (&rs)[RPW]) {
-#pragma unroll
-          for (int jj = 0; jj < RPW; ++jj) load_one(tile, jj, rs[jj]);
-        };
-        auto store_set = [&](int tile, const u32x2 (&rs)[RPW]) {
-          uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes + wave_u * RPW * kRowPitch;
-#pragma unroll
-          for (int jj = 0; jj < RPW; ++jj) {
-            if constexpr (PACKED)
-              packed_store_row(dst + jj * kRowPitch, lane, rs[jj]);
-            else
-              *(u32x4*)(dst + jj * kRowPitch + lane * 16) = widen_e4m3fn_x8(rs[jj]);
-          }
+        auto store_one = [&](int tile, int jj) {
+          uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes +
+                         (wave_u * RPW + jj) * kRowPitch;
+          if constexpr (PACKED)
+            packed_store_row(dst, lane, rs[jj]);
+          else
+            *(u32x4*)(dst + lane * 16) = widen_e4m3fn_x8(rs[jj]);
         };
         fetch_rows(0, rows);
-        load_set(0, rs0);
-        fetch_rows(1, rows);
-        load_set(1, rs1);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) load_one(0, jj);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) store_one(0, jj);
+        fetch_rows(min(1, ntiles - 1), rows);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) load_one(1, jj);
         fetch_rows(min(2, ntiles - 1), rows);
-        store_set(0, rs0);
-        // One iteration; PAR = it & 1 names the register set of tile it+2.
-        // QK: tile it exists; LOAD / STORE: load tile it+2, store tile it+1.
-        // All are compile-time so that the loop body has no branches and
-        // the compiler's load waits stay exact (at a branch merge it would
-        // wait for every load).  Loads past the last tile re-read valid
-        // rows (fetch_rows clamps), which hit in L2.
-        auto iteration = [&](auto par, auto pv, auto qk_on, auto load_on, auto store_on,
-                             int it) {
-          constexpr bool kOdd = decltype(par)::value;
+        // One iteration.  QK: tile it exists; MOVE: store tile it+1 and load
+        // tile it+2.  Both are compile-time so that the loop body has no
+        // branches and the compiler's load waits stay exact (at a branch
+        // merge it would wait for every load).  Rows past the last tile
+        // re-read valid rows (fetch_rows clamps), which hit in L2, and are
+        // stored to a stage that no S^T reads.
+        auto iteration = [&](auto pv, auto qk_on, auto move_on, int it) {
           constexpr bool kQK = decltype(qk_on)::value;
-          constexpr bool kLoad = decltype(load_on)::value;
-          constexpr bool kStore = decltype(store_on)::value;
-          u32x2 (&rs_next)[RPW] = kOdd ? rs1 : rs0;    // tile it+2
-          u32x2 (&rs_land)[RPW] = kOdd ? rs0 : rs1;    // tile it+1
+          constexpr bool kMove = decltype(move_on)::value;
           // tile it is in LDS, P^T of tile it-1 is written, and the readers
           // of the previous iteration are done
           __syncthreads();
@@ -1359,7 +1358,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           f32x16 sv;
           if constexpr (kQK) {
             sv = qk(stage(it), [&](int kk) {
-              if (kLoad && (kk & 3) == 3) load_one(it + 2, kk >> 2, rs_next[kk >> 2]);
+              if (kMove && (kk & 3) == 1) store_one(it + 1, kk >> 2);
+              if (kMove && (kk & 3) == 3) load_one(it + 2, kk >> 2);
             }, [] {});
             mfma_qk_drain(sv);
             mask_tail(sv, it);
@@ -1367,8 +1367,6 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
           }
-          // (the O^T operands are read after the S^T MFMAs here: the two
-          // register sets leave no room to hold them across S^T)
           bf16x8 pfr[NHB], vfr[kVLead];
           if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
           // the row addresses of tile it+3 (those of tile it+2 were used by
@@ -1377,26 +1375,22 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           int code = 0;
           uint64_t addr = 0;
           step_block(pv, vt, pr, pfr, vfr, sv, p_lds + (it & 1) * kPBuf, [&](int k) {
-            if constexpr (kLoad) {
+            if constexpr (kMove) {
               if (k == 4) code = row_code(min(it + 3, ntiles - 1));
               if (k == 20) addr = row_addr(code);
               if (k >= 21 && k < 21 + RPW) rows[k - 21] = row_of_lane(addr, k - 21);
             }
           });
-          if constexpr (kStore) store_set(it + 1, rs_land);
         };
         using T_ = BoolC<true>;
         using F_ = BoolC<false>;
-        iteration(F_{}, F_{}, T_{}, T_{}, T_{}, 0);
-        // ntiles is even: pairs of iterations with every step, then the last
-        // tile's iteration (nothing left to load or store) and the drain
+        // the first tile (with one tile only, its moves fill an unused
+        // stage), every later tile but the last, the last, and the drain
+        iteration(F_{}, T_{}, T_{}, 0);
         int it = 1;
-        for (; it + 1 < ntiles; it += 2) {
-          iteration(T_{}, T_{}, T_{}, T_{}, T_{}, it);
-          iteration(F_{}, T_{}, T_{}, T_{}, T_{}, it + 1);
-        }
-        iteration(T_{}, T_{}, T_{}, F_{}, F_{}, ntiles - 1);
-        iteration(F_{}, T_{}, F_{}, F_{}, F_{}, ntiles);
+        for (; it + 1 < ntiles; ++it) iteration(T_{}, T_{}, T_{}, it);
+        if (ntiles > 1) iteration(T_{}, T_{}, F_{}, ntiles - 1);
+        iteration(T_{}, F_{}, F_{}, ntiles);
       }
     } else if (ntiles > 0) {
       // LDS-DMA gather, two tiles ahead.
