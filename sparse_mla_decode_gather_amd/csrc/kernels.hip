@@ -43,6 +43,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -247,50 +248,50 @@ typedef int32_t __attribute__((address_space(1))) global_i32;
 // one UE8M0 scale byte per 56 NoPE dims (bytes 576..583); NoPE dim d is
 // E4M3FN(byte d) * 2^(scale[d / 56] - 127).
 //
-// In the kernels a packed row reaches its BF16 LDS tile row in two parts:
-//  * lanes 0..55 load the 8 NoPE codes of dims [8 lane, 8 lane + 8) through
-//    registers, exactly as per-tensor FP8 rows do, and widen them with their
-//    block's scale when the tile is written (E4M3FN times a power of two is
-//    exactly a BF16 value in the normal range);
-//  * the RoPE dims (already BF16) and the scale bytes go by one 9-lane
-//    LDS-DMA straight into the tile row: lane j < 8 moves bytes
-//    [448 + 16 j, +16) to row offset 896 + 16 j, lane 8 moves bytes
-//    [568, 584) (the last RoPE dims again, then the 8 scale bytes) to the
-//    row's padding at offset 1024, so the scale bytes sit at 1032..1039.
+// In the kernels every lane of a wave loads 16 bytes of a packed row in two
+// 8-byte halves and writes 16 bytes of its BF16 LDS tile row at 16 lane:
+//  * lane L < 56 loads the 8 NoPE codes of dims [8 L, 8 L + 8) and the 8
+//    scale bytes, picks the scale of its block (L / 7) and writes the codes
+//    widened with it (E4M3FN times a power of two is exactly a BF16 value in
+//    the normal range);
+//  * lane 56 + i loads the RoPE bytes [448 + 16 i, +16), which are BF16
+//    already, and writes them as they are, to tile row bytes 896 + 16 i.
+// So the store is one full-wave write per row, with no branch and no exec
+// mask change.
 constexpr int kPackedRowBytes = 584;
 constexpr int kPackedNopeLanes = 56;       // lanes holding 8 NoPE codes each
 constexpr int kPackedBlockLanes = 7;       // 56 dims per scale = 7 lanes
-constexpr int kPackedScaleLds = 1032;      // scale bytes in the LDS row
-static_assert(kPackedScaleLds + 8 <= kRowPitch, "scale bytes fit the row padding");
+constexpr int kPackedScaleOff = 576;       // first scale byte in the row
+constexpr int kPackedRopeOff = 448;        // first RoPE byte in the row
+static_assert(kPackedNopeLanes * 16 == 2 * kPackedRopeOff,
+              "the RoPE lanes' 16 lane bytes are the RoPE dims' tile offsets");
 
-// The RoPE dims and scale bytes of one packed row into its LDS tile row
-// (lds_row = the row's LDS byte address).  Only lanes 0..8 take part: the
-// exec mask is narrowed and restored inside the statement, so the compiler
-// sees one straight-line instruction group.  `tail_off` is the lane's byte
-// offset in the row (448 + 16 lane for lanes 0..7, 568 for lane 8).  The
-// buffer resource covers exactly the row.
-__device__ __forceinline__ void packed_tail_dma(const uint8_t* row, uint32_t tail_off,
-                                                uint32_t lds_row) {
+// The lane's two row byte offsets and its scale-byte selector.
+struct PackedLane {
+  uint32_t off_a, off_b;   // the two 8-byte halves
+  uint32_t sel;            // v_perm selector: byte L / 7 of the scales, zeros above
+  bool nope;               // the lane holds NoPE codes
+};
+__device__ __forceinline__ PackedLane packed_lane(int lane) {
+  PackedLane pl;
+  pl.nope = lane < kPackedNopeLanes;
+  const uint32_t rope = kPackedRopeOff + 16u * (uint32_t)(lane - kPackedNopeLanes);
+  pl.off_a = pl.nope ? 8u * (uint32_t)lane : rope;
+  pl.off_b = pl.nope ? (uint32_t)kPackedScaleOff : rope + 8u;
+  pl.sel = 0x0c0c0c00u | ((uint32_t)(lane / kPackedBlockLanes) & 7u);
+  return pl;
+}
+
+// The lane's 16 bytes of a packed row, through a buffer resource that covers
+// exactly the row.
+__device__ __forceinline__ u32x4 packed_load_row(const uint8_t* row, const PackedLane& pl) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)row, (short)0, kPackedRowBytes, kRawBufferWord3);
-  uint64_t saved_exec;
-  uint32_t saved_m0;
-  // s_nop 4: the row address may come from a VALU write of an SGPR
-  // (v_readlane); s_nop 1 after the EXEC write and s_nop 0 after the M0
-  // write before the LDS-DMA.
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b64 %0, exec\n\t"
-      "s_mov_b64 exec, 0x1ff\n\t"
-      "s_mov_b32 %1, m0\n\t"
-      "s_mov_b32 m0, %4\n\t"
-      "s_nop 1\n\t"
-      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "s_mov_b64 exec, %0"
-      : "=&s"(saved_exec), "=&s"(saved_m0)
-      : "v"(tail_off), "s"(rs), "s"(lds_row + 896u)
-      : "memory");
+  const u32x2 a = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)pl.off_a, 0, 0));
+  const u32x2 b = __builtin_bit_cast(
+      u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, (int)pl.off_b, 0, 0));
+  return u32x4{a[0], a[1], b[0], b[1]};
 }
 
 // UE8M0 scale byte -> the binary32 power of two 2^(e - 127) (e = 255: NaN).
@@ -310,18 +311,16 @@ __device__ __forceinline__ u32x4 widen_e4m3fn_x8_scaled(u32x2 v, float scale) {
   return r;
 }
 
-// The lane's NoPE codes (registers) of a packed row into its LDS tile row,
-// widened with the scale byte the row's DMA put in the padding.  The scale
-// read takes its address through `codes`, so it cannot be scheduled before
-// the codes (and, the DMA having been issued first, the scale bytes) have
-// landed.  Lanes 56..63 hold RoPE bytes the DMA already placed: no store.
-__device__ __forceinline__ void packed_store_row(uint8_t* lds_row, int lane, u32x2 codes) {
-  uint32_t dep = codes[0];
-  asm volatile("v_and_b32 %0, 0, %0" : "+v"(dep));
-  if (lane < kPackedNopeLanes) {
-    const uint32_t e = lds_row[kPackedScaleLds + lane / kPackedBlockLanes + dep];
-    *(u32x4*)(lds_row + lane * 16) = widen_e4m3fn_x8_scaled(codes, ue8m0_scale(e));
-  }
+// The 16 bytes the lane writes to its tile row at 16 lane: NoPE lanes
+// their codes widened with the block's scale (byte sel of the scale bytes
+// in v[2..3]), RoPE lanes the bytes as loaded.
+__device__ __forceinline__ u32x4 packed_tile_bytes(u32x4 v, const PackedLane& pl) {
+  const uint32_t e = __builtin_amdgcn_perm(v[3], v[2], pl.sel);
+  const u32x4 w = widen_e4m3fn_x8_scaled(u32x2{v[0], v[1]}, ue8m0_scale(e));
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pl.nope ? w[i] : v[i];
+  return r;
 }
 
 __device__ __forceinline__ void record_error(int32_t* err, int code, int t,
@@ -763,12 +762,10 @@ void decode_kernel(DecodeParams p) {
       // after its O^T MFMAs, into the stage tile it-1 used.
       static_assert(KV_FP8, "register staging serves FP8 rows");
       constexpr int VW = 2;                       // dwords per lane per row
-      typedef u32x2 stage_t;
+      typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
       const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
       const uint32_t lane_off = (uint32_t)lane * (VW * 4);
-      // packed rows: the lane's byte offset of the RoPE / scale DMA
-      const uint32_t tail_off = lane < 8 ? 448u + 16u * (uint32_t)lane : 568u;
-      const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
+      const PackedLane pl = packed_lane(lane);   // packed rows only
       stage_t st[RPW];
       auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
         const int s0 = tile * kTile + wave_u * RPW;
@@ -785,18 +782,16 @@ void decode_kernel(DecodeParams p) {
         code = (s0 + jj < n_act) ? code : last_code;
         const uint8_t* base = code < 0 ? p.comp : p.swa;
         const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
-        if constexpr (PACKED)
-          packed_tail_dma(row, tail_off,
-                          lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes +
-                                                (wave_u * RPW + jj) * kRowPitch));
-        st[jj] = load_row8(row, lane_off);
+        if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
+        else st[jj] = load_row8(row, lane_off);
       };
       auto store = [&](int tile) {
         uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
 #pragma unroll
         for (int jj = 0; jj < RPW; ++jj) {
           if constexpr (PACKED) {
-            packed_store_row(dst + (wave_u * RPW + jj) * kRowPitch, lane, st[jj]);
+            *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
+                packed_tile_bytes(st[jj], pl);
           } else {
             u32x4 v;
             if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
@@ -1308,27 +1303,20 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         // tile it+2 is loaded into it, so every load has about one tile of
         // MFMA work to land.  These are ordinary loads, so the compiler's
         // own waits are exact.
-        u32x2 rs[RPW];
+        std::conditional_t<PACKED, u32x4, u32x2> rs[RPW];
         const uint8_t* rows[RPW];
         const uint32_t lane_off8 = (uint32_t)lane * 8u;
-        // packed rows: the lane's byte offset of the RoPE / scale DMA
-        const uint32_t tail_off = lane < 8 ? 448u + 16u * (uint32_t)lane : 568u;
-        // LDS byte address of the wave's row jj of `tile`
-        auto lds_row_addr = [&](int tile, int jj) -> uint32_t {
-          return lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes) +
-                 (uint32_t)((wave_u * RPW + jj) * kRowPitch);
-        };
-        // one row of `tile` into its register (a packed row's RoPE dims and
-        // scale bytes first go straight to LDS)
+        const PackedLane pl = packed_lane(lane);   // packed rows only
+        // one row of `tile` into its registers
         auto load_one = [&](int tile, int jj) {
-          if constexpr (PACKED) packed_tail_dma(rows[jj], tail_off, lds_row_addr(tile, jj));
-          rs[jj] = load_row8(rows[jj], lane_off8);
+          if constexpr (PACKED) rs[jj] = packed_load_row(rows[jj], pl);
+          else rs[jj] = load_row8(rows[jj], lane_off8);
         };
         auto store_one = [&](int tile, int jj) {
           uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes +
                          (wave_u * RPW + jj) * kRowPitch;
           if constexpr (PACKED)
-            packed_store_row(dst, lane, rs[jj]);
+            *(u32x4*)(dst + lane * 16) = packed_tile_bytes(rs[jj], pl);
           else
             *(u32x4*)(dst + lane * 16) = widen_e4m3fn_x8(rs[jj]);
         };
