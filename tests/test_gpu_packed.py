@@ -3,9 +3,9 @@ against the oracle's decode of the same bytes.
 
 * Single active slot, no sink: the output is the decoded row itself, which
   is exactly a BF16 row, so the GPU result must equal it bit for bit --
-  this pins the byte layout, the per-block scales and the RoPE / scale DMA
-  of the kernels, for both head counts, split and unsplit, at the first and
-  last rows of both pools and for scale bytes far from 127.
+  this pins the byte layout, the per-block scale selection and the RoPE
+  lanes' stores of the kernels, for both head counts, split and unsplit, at
+  the first and last rows of both pools and for scale bytes far from 127.
 * Element-wise parity (the FP8 bar, 3e-2 + 3e-2*|ref|, LSE 1e-3) with
   ragged lengths, -1 slots, several table segments, padded rows, the
   two-segment and page-table forms, and every token of the full-size
@@ -115,8 +115,8 @@ def test_packed_edges_match_oracle(H):
 
 @pytest.mark.parametrize("H", [64, 128])
 def test_packed_padded_rows(H):
-    """Rows 592 bytes apart (8 bytes of padding): every load and DMA starts
-    at its row's own address."""
+    """Rows 592 bytes apart (8 bytes of padding): every load starts at its
+    row's own address."""
     need_gpu()
     rng = np.random.default_rng(4)
 
