@@ -1444,12 +1444,19 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         bf16x8 pfr[NHB], vfr[kVLead];
         f32x16 sv;
         if constexpr (kSteady) {
-          // the first S^T operand reads go out before the O^T operand reads
+          // The first O^T operands are read inside the S^T MFMAs, spread
+          // out (P^T after MFMAs 8..11, V^T after MFMAs 20, 22, 24, 26):
+          // read before the S^T chain they held 32 registers across it, and
+          // their LDS trips sat between the first S^T operand reads.
           const uint32_t tile_base = lds_base + (uint32_t)(((it + 2) % NSTAGE) * kTileBytes) +
                                      (uint32_t)(wave_u * RPW * kRowPitch);
+          const uint8_t* vt = stage(it - 1);
           sv = qk(stage(it), [&](int kk) {
             if ((kk & 3) == 3) issue_row_settled(tile_base, kk >> 2, rows[kk >> 2]);
-          }, [&] { pv_prefetch(stage(it - 1), pr, pfr, vfr); });
+            if (kk >= 8 && kk < 8 + NHB) pfr[kk - 8] = pfrag(pr, 0, kk - 8);
+            if (kk >= 20 && kk < 20 + 2 * kVLead && (kk & 1) == 0)
+              vfr[(kk - 20) >> 1] = vfrag(vt, (kk - 20) >> 1);
+          }, [] {});
           mfma_qk_drain(sv);
         } else if (it < ntiles) {
           if constexpr (!GATHER_ONLY) pv_prefetch(stage(it - 1), pr, pfr, vfr);
