@@ -1344,19 +1344,26 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           const u32x4* pr = p_lds + ((it + 1) & 1) * kPBuf;      // tile it-1
           const uint8_t* vt = kv_lds + ((it + NSTAGE - 1) % NSTAGE) * kTileBytes;
           f32x16 sv;
+          // The first O^T operands of tile it-1 are read inside the S^T
+          // MFMAs (P^T after MFMAs 16..19, V^T after 24, 26, 28).
+          bf16x8 pfr[NHB], vfr[kVLead];
           if constexpr (kQK) {
             sv = qk(stage(it), [&](int kk) {
               if (kMove && (kk & 3) == 1) store_one(it + 1, kk >> 2);
               if (kMove && (kk & 3) == 3) load_one(it + 2, kk >> 2);
+              if constexpr (decltype(pv)::value) {
+                if (kk >= 16 && kk < 16 + NHB) pfr[kk - 16] = pfrag(pr, 0, kk - 16);
+                if (kk >= 24 && kk < 24 + 2 * kVLead && ((kk - 24) & 1) == 0)
+                  vfr[(kk - 24) >> 1] = vfrag(vt, (kk - 24) >> 1);
+              }
             }, [] {});
             mfma_qk_drain(sv);
             mask_tail(sv, it);
           } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
+            if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
           }
-          bf16x8 pfr[NHB], vfr[kVLead];
-          if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
           // the row addresses of tile it+3 (those of tile it+2 were used by
           // the loads above): slot code under the first MFMAs, readouts
           // between the last ones, which have no softmax work beside them
