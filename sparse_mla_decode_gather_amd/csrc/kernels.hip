@@ -1120,7 +1120,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
     // first use; otherwise P^T(1, hb) replaces P^T(0, hb) right after its
     // last use, four MFMAs before it is needed.
     constexpr bool kP1Early = !KV_FP8;
-    float smax = 0.f, neg_m = 0.f, lsum = 0.f, pprev = 0.f;
+    float smax = 0.f, tmax = 0.f, lsum = 0.f, mx[5];
+    bool need = false;
     u32x4 pk[2];
     bf16x8 pfr1[NHB];
 #pragma unroll
@@ -1138,30 +1139,45 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           if (f == 3) pfr[hb] = pfrag(pr, 1, hb);
         }
       }
+      // The softmax of the current tile, spread so that no step waits for
+      // a result of the same MFMA slot: the max as a tree (k = 0, 1), the
+      // reference max (k = 2, 3), then value j's logit at k = 3 + j, its
+      // exponential at k = 4 + j, its sum and BF16 pair at k = 5 + j, and
+      // P^T at k = 21.
       if (k == 0) {
-        smax = sv[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) smax = fmaxf(smax, sv[i]);
+        mx[0] = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+        mx[1] = fmaxf(fmaxf(sv[3], sv[4]), sv[5]);
+        mx[2] = fmaxf(fmaxf(sv[6], sv[7]), sv[8]);
+        mx[3] = fmaxf(fmaxf(sv[9], sv[10]), sv[11]);
+        mx[4] = fmaxf(fmaxf(sv[12], sv[13]), sv[14]);
       } else if (k == 1) {
-#pragma unroll
-        for (int i = 8; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+        smax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), sv[15]), fmaxf(fmaxf(mx[2], mx[3]), mx[4]));
         smax = max_with_other_half(smax);
       } else if (k == 2) {
         // The reference max is set by the first tile and then left alone,
         // so O is never rescaled inside the loop (see decode_kernel).
-        const float tmax = smax * p.scale_log2;     // scale_log2 > 0
+        tmax = smax * p.scale_log2;     // scale_log2 > 0
         m_run = (m_run == -INFINITY) ? tmax : m_run;
-        const bool need = tmax > m_run + kRefSlack;
+        need = tmax > m_run + kRefSlack;
+      }
+      if (k == 3) {
         m_run = need ? tmax : m_run;
         need_sticky |= need;
-        neg_m = -m_run;
-      } else if (k >= 3 && k < 19) {
-        const int i = k - 3;
-        const float pi = fast_exp2(__builtin_fmaf(sv[i], p.scale_log2, neg_m));
-        lsum += pi;
-        if (i & 1) pk[i >> 3][(i & 7) >> 1] = pack_bf16x2(pprev, pi);
-        pprev = pi;
-      } else if (k == 19) {
+      }
+      if (k >= 3 && k < 19) {
+        const int j = k - 3;
+        sv[j] = __builtin_fmaf(sv[j], p.scale_log2, -m_run);
+      }
+      if (k >= 4 && k < 20) {
+        const int j = k - 4;
+        sv[j] = fast_exp2(sv[j]);
+      }
+      if (k >= 5 && k < 21) {
+        const int j = k - 5;
+        lsum += sv[j];
+        if (j & 1) pk[j >> 3][(j & 7) >> 1] = pack_bf16x2(sv[j - 1], sv[j]);
+      }
+      if (k == 21) {
         pw[(wave * 2 + 0) * 64 + lane] = pk[0];
         pw[(wave * 2 + 1) * 64 + lane] = pk[1];
         l_run += lsum;
@@ -1372,8 +1388,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           step_block(pv, vt, pr, pfr, vfr, sv, p_lds + (it & 1) * kPBuf, [&](int k) {
             if constexpr (kMove) {
               if (k == 4) code = row_code(min(it + 3, ntiles - 1));
-              if (k == 20) addr = row_addr(code);
-              if (k >= 21 && k < 21 + RPW) rows[k - 21] = row_of_lane(addr, k - 21);
+              if (k == 23) addr = row_addr(code);
+              if (k >= 24 && k < 24 + RPW) rows[k - 24] = row_of_lane(addr, k - 24);
             }
           });
         };
@@ -1483,8 +1499,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
           step_block(BoolC<true>{}, stage(it - 1), pr, pfr, vfr, sv,
                      p_lds + (it & 1) * kPBuf, [&](int k) {
                        if (k == 4) code = row_code(min(it + 3, ntiles - 1));
-                       if (k == 20) addr = row_addr(code);
-                       if (k >= 21 && k < 21 + RPW) rows[k - 21] = row_of_lane(addr, k - 21);
+                       if (k == 23) addr = row_addr(code);
+                       if (k >= 24 && k < 24 + RPW) rows[k - 24] = row_of_lane(addr, k - 24);
                      });
         } else {
           if constexpr (!GATHER_ONLY)
@@ -1523,11 +1539,6 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
   } while (again);
   if constexpr (GATHER_ONLY) return;
-  // Packed rows: the last iterations may have issued RoPE / scale DMAs for
-  // clamped (re-read) rows of no tile; they must land before the epilogue
-  // reuses the tile memory.
-  if constexpr (PACKED) wait_vmcnt<0>();
-
   // ---- epilogue: the head owner finishes its head's normaliser ------------
   {
     float l = l_run + __shfl_xor(l_run, 32);
