@@ -1116,9 +1116,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
                         f32x16 sv, u32x4* pw, auto&& every) {
     constexpr bool kPV = decltype(do_pv)::value;
     // P^T operands of the second 16-row half: with a register set of their
-    // own (kP1Early, BF16 rows) they are read twelve MFMAs ahead of their
-    // first use; otherwise P^T(1, hb) replaces P^T(0, hb) right after its
-    // last use, four MFMAs before it is needed.
+    // own (kP1Early, BF16 rows) they are read eight MFMAs ahead of their
+    // first use; otherwise (FP8 rows, which have no registers to spare)
+    // P^T(1, hb) replaces P^T(0, hb) right after its last use, four MFMAs
+    // before it is needed.
     constexpr bool kP1Early = !KV_FP8;
     float smax = 0.f, tmax = 0.f, lsum = 0.f, mx[5];
     bool need = false;
