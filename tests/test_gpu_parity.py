@@ -270,12 +270,13 @@ def test_wide_table_multiple_segments():
                                   (64, W.FP8)])
 def test_fp8_rows_edges_segments_and_restarts(H, q):
     """FP8 rows at H=128 take the register-staged path of the H=128 kernel
-    (two register sets, an extra all-masked tile when the tile count is
-    odd); at H=64 they are loaded through registers one tile ahead; in both
-    kernels FP8 rows (and FP8 q) are widened exactly to BF16 and multiplied
-    on the BF16 MFMA.  Ragged and tiny
-    lengths give odd, single and empty tile counts; K=5000 crosses
-    segments; wide logits force restarts."""
+    (one register set: each row of tile i+1 is stored and the same row of
+    tile i+2 loaded inside the S^T MFMAs of tile i; the first tile, the last
+    and the drain are separate compile-time iterations); at H=64 they are
+    loaded through registers one tile ahead; in both kernels FP8 rows (and
+    FP8 q) are widened exactly to BF16 and multiplied on the BF16 MFMA.
+    Ragged and tiny lengths give odd, single and empty tile counts; K=5000
+    crosses segments; wide logits force restarts."""
     need_gpu()
     qc = L.DTYPE_FP8_E4M3FN if q == W.FP8 else L.DTYPE_BF16
     kc = L.DTYPE_FP8_E4M3FN
