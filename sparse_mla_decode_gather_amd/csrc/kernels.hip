@@ -910,9 +910,9 @@ void decode_kernel(DecodeParams p) {
 // one VALU pass (one row per lane) and read out into SGPRs, and each row
 // costs one load instruction.
 
-// KV_FP8: E4M3FN rows go through registers (two tiles ahead, in two
-// register sets) and are widened to BF16 as they are written to LDS; BF16
-// rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
+// KV_FP8: E4M3FN rows (or packed rows, PACKED) go through one register
+// set, two tiles ahead, and are widened to BF16 as they are written to LDS;
+// BF16 rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false,
