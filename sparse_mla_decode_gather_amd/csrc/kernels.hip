@@ -612,7 +612,8 @@ void decode_kernel(DecodeParams p) {
   };
   // O^T += V^T P^T for a tile: step k covers rows [16h, 16h+16) (h = k/16)
   // of d-block db = k%16.
-  auto pv = [&](const uint8_t* tb, const bf16x8 (&pf)[2]) {
+  // O^T += V^T P^T for the tile at tb; `every(k)` runs after MFMA k.
+  auto pv = [&](const uint8_t* tb, const bf16x8 (&pf)[2], auto&& every) {
     auto vfrag = [&](int k) -> bf16x8 {
       const uint8_t* vb = tb + tr_off + (16 * (k >> 4)) * kRowPitch + (k & 15) * 64;
       const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -631,9 +632,11 @@ void decode_kernel(DecodeParams p) {
       o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k % kLead], pf[k >> 4],
                                                          o[k & 15], 0, 0, 0);
       if (k + kLead < 32) v[k % kLead] = vfrag(k + kLead);
+      every(k);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  auto pv_no_hook = [](int) {};
 
   bool again;
   do {
@@ -750,7 +753,7 @@ void decode_kernel(DecodeParams p) {
         });
         bf16x8 pf[2];
         softmax(sv, n_in(it), pf, steady);
-        pv(stage(it), pf);
+        pv(stage(it), pf, pv_no_hook);
       };
       int it = 0;
       for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
@@ -785,20 +788,21 @@ void decode_kernel(DecodeParams p) {
         if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
         else st[jj] = load_row8(row, lane_off);
       };
-      auto store = [&](int tile) {
+      auto store_row = [&](int tile, int jj) {
         uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
-#pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) {
-          if constexpr (PACKED) {
-            *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
-                packed_tile_bytes(st[jj], pl);
-          } else {
-            u32x4 v;
-            if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
-            else v = st[jj];
-            *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
-          }
+        if constexpr (PACKED) {
+          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
+              packed_tile_bytes(st[jj], pl);
+        } else {
+          u32x4 v;
+          if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
+          else v = st[jj];
+          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
         }
+      };
+      auto store = [&](int tile) {
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) store_row(tile, jj);
       };
       // prologue: tiles 0 .. NSTAGE-2 into their stages
       for (int tl = 0; tl < min(NSTAGE - 1, ntiles); ++tl) {
@@ -824,8 +828,18 @@ void decode_kernel(DecodeParams p) {
         });
         bf16x8 pf[2];
         softmax(sv, n_in(it), pf, steady);
-        pv(stage(it), pf);
-        if (do_load) store(nxt);
+        if constexpr (kSteady) {
+          // The next tile's rows go to its stage (the one tile it-1 used,
+          // free since the barrier) between the O^T MFMAs, one row per two
+          // MFMAs: their loads went out during the S^T MFMAs.
+          static_assert(2 * RPW <= 32, "a row per two O^T MFMAs");
+          pv(stage(it), pf, [&](int k) {
+            if ((k & 1) == 0 && (k >> 1) < RPW) store_row(nxt, k >> 1);
+          });
+        } else {
+          pv(stage(it), pf, pv_no_hook);
+          if (do_load) store(nxt);
+        }
       };
       int it = 0;
       for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
