@@ -11,6 +11,15 @@ A step is one sparse_mla_decode call (planner + split kernel [+ combine]).
 Each launch is bracketed by HIP events on the stream it runs on, so the
 average launch duration, gathered bytes and FLOPs give the roofline numbers.
 
+Every timed region is preceded by the same step run back to back for about
+200 ms of GPU time (--settle-ms), then the W warmup steps.  After an idle of
+about 10 ms or more the board's power management runs the first few
+launches at full clock, cuts the clock steeply a few milliseconds into the
+burst and restores it over some tens of milliseconds of sustained load; a
+short timed region right after the idle measures that transient rather
+than the kernel's sustained rate.  The line also carries the rate of the
+same W + K steps right after a 50 ms idle (``after_idle``), unsettled.
+
 Besides the headline numbers the line carries: the pure-gather rate on the
 same tables (sparse_mla_gather_only: compaction and row loads only, the
 attainable gather bandwidth), the rate of the same call in the two-segment
@@ -29,8 +38,9 @@ rows) with their default plans and roofline fractions, and the roofline
 fraction against peaks measured on the box.
 
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
---no-cpu-baseline, --headline-only (skip the sweep, the other
-configurations and the measured peaks), --only-workload NAME.
+--settle-ms, --no-cpu-baseline, --headline-only (the headline's settled
+timed region alone, for profilers: its K launches are the headline kernel's
+last K dispatches), --only-workload NAME.
 """
 
 import argparse
@@ -47,6 +57,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA, published
 ROW_BYTES = 1024                # one BF16 row of 512 elements
 COUNTERS = os.path.join(ROOT, "profiles", "decode_long_context_T512_traffic.txt")
+SETTLE_MS = 200.0               # back-to-back GPU time before each timed region
 
 
 def active_slots_per_token(w):
@@ -82,13 +93,12 @@ def time_launches(fn, steps, warmup, stream):
     """Run fn() warmup+steps times; HIP events around each timed launch on
     ``stream``.  Returns (total ms over the timed region, per-launch ms)."""
     import torch
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(
         enable_timing=True)
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
     start.record(stream)
     for a, b in evs:
@@ -99,6 +109,38 @@ def time_launches(fn, steps, warmup, stream):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in evs]
     return start.elapsed_time(end), per
+
+
+def settle(fn, stream, ms):
+    """Run fn() back to back for about ``ms`` of GPU time with no host wait
+    in between, so that the timed region that follows sees the clock of
+    sustained load rather than the power-management transient after an
+    idle.  The launch count comes from the fastest of three timed launches
+    after an untimed one (a process's first launch of a kernel also loads
+    its code).  Returns the launches run."""
+    import torch
+    if ms <= 0:
+        return 0
+    fn()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b))
+    n = int(min(max(ms / max(best, 1e-3), 1.0), 20000))
+    for _ in range(n):
+        fn()
+    return n + 4
+
+
+def time_settled(fn, steps, warmup, stream, ms):
+    """settle() then time_launches()."""
+    settle(fn, stream, ms)
+    return time_launches(fn, steps, warmup, stream)
 
 
 def time_cold(fn, iters, stream):
@@ -262,11 +304,11 @@ ROW_BYTES_BY_KV = {"bf16": 1024, "fp8_e4m3fn": 512, "packed_fp8_584": 584}
 WORKLOAD_NAMES = ("tiny", "batched_sinks", "fp8", "spec_decode", "packed")
 
 
-def other_workloads(stream, only=None):
+def other_workloads(stream, only=None, settle_ms=SETTLE_MS):
     """The other configurations with their default plans: per-launch time
-    (HIP events around 30 back-to-back launches, and HIP-graph replays),
-    gathered bytes and FLOPs of the active slots, and the fraction of the
-    roofline max(bytes / HBM peak, FLOPs / MFMA peak).  FP8 rows are widened
+    (HIP events around 30 back-to-back launches after settle(), and HIP-graph
+    replays), gathered bytes and FLOPs of the active slots, and the fraction
+    of the roofline max(bytes / HBM peak, FLOPs / MFMA peak).  FP8 rows are widened
     to BF16 and multiplied on BF16 MFMA, so BF16 is the MFMA peak."""
     import torch
     from sparse_mla_decode_gather_amd import lib, workloads as W
@@ -289,7 +331,7 @@ def other_workloads(stream, only=None):
 
         def st(w=w, out=out, lse=lse, plan=plan, ws=ws):
             lib.decode_workload(w, out, lse, plan=plan, workspace=ws)
-        _, per = time_launches(st, 30, 5, stream)
+        _, per = time_settled(st, 30, 5, stream, settle_ms)
         avg = sum(per) / len(per)
         gms = time_graph(st)
         t_roof = max(gathered / (HBM_PEAK_GBPS * 1e9),
@@ -308,61 +350,19 @@ def other_workloads(stream, only=None):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--T", type=int, default=512)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--headline-only", action="store_true",
-                    help="skip the T sweep, the other configurations and the "
-                         "measured peaks (a short command to run under a "
-                         "profiler); by default the line carries all of them")
-    ap.add_argument("--only-workload", choices=WORKLOAD_NAMES,
-                    help="time only this other configuration (as the default line "
-                         "does) and print its record instead of the headline "
-                         "line: a short command to run under a kernel tracer")
-    ap.add_argument("--calibration-copy", action="store_true",
-                    help="after timing, run a plain 1 GiB device copy three "
-                         "times (known bytes) for counter calibration")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py: the decode is measured on one GPU; --gpus {args.gpus} is "
-              "not supported (tokens would shard across GPUs with no exchange, so "
-              "the per-GPU rate is the one-GPU rate)", file=sys.stderr)
-        sys.exit(2)
-
+def side_measurements(w, step, plan, ws, out, lse, args, stream):
+    """The headline's companions on the same tables: the pure-gather rate,
+    the two-segment and page-table forms against the combined call, the
+    combined-table builder and the cold-cache rate."""
     import torch
-    from sparse_mla_decode_gather_amd import lib, workloads as W
-
-    lib.load()
-    torch.cuda.set_device(0)
-    stream = torch.cuda.current_stream()
-    if args.only_workload:
-        rec = other_workloads(stream, only=args.only_workload)[args.only_workload]
-        print(json.dumps({"workload": args.only_workload, **rec}), flush=True)
-        return
-    w = W.make_long_context(args.T, "cuda", seed=4000 + args.T)
-    n_act = active_slots_per_token(w)
+    from sparse_mla_decode_gather_amd import lib
     T = w.T
-    out = torch.empty((T, w.H, 512), dtype=torch.bfloat16, device="cuda")
-    lse = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
-    plan = lib.plan_splits(T, w.H, w.K)
-    ws = lib.alloc_workspace(plan, T, w.H)
-
-    def step():
-        lib.decode(w.q, w.swa_pool, w.comp_pool, w.indices, out, out_lse=lse,
-                   topk_lens=w.topk_lens, seq_lens=w.seq_lens, sinks=w.sinks,
-                   bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
-                   lse_scale=w.lse_scale, plan=plan, workspace=ws, stream=stream)
-
-    total_ms, per = time_launches(step, args.steps, args.warmup, stream)
 
     def gather_step():
         lib.gather_only(w.q, w.swa_pool, w.comp_pool, w.indices,
                         topk_lens=w.topk_lens, plan=plan, stream=stream)
-    _, gper = time_launches(gather_step, max(args.steps // 2, 5), 3, stream)
+    _, gper = time_settled(gather_step, max(args.steps // 2, 5), 3, stream,
+                           args.settle_ms)
     # the same tables in the two-segment form (128-column SWA table with its
     # length, 1920-column compressed table with its length)
     swa_tab, extra_tab = w.indices[:, :128], w.indices[:, 128:]
@@ -377,6 +377,7 @@ def main():
                             lse_scale=w.lse_scale, plan=plan, workspace=ws,
                             stream=stream)
     # alternate with the combined call so that both see the same clock
+    settle(step, stream, args.settle_ms)
     sper, cper = [], []
     for _ in range(4):
         sper += time_launches(seg_step, 8, 2, stream)[1]
@@ -398,6 +399,7 @@ def main():
                          bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
                          lse_scale=w.lse_scale, plan=plan, workspace=ws,
                          stream=stream)
+    settle(step, stream, args.settle_ms)
     pper, cper2 = [], []
     for _ in range(4):
         pper += time_launches(paged_step, 8, 2, stream)[1]
@@ -425,6 +427,88 @@ def main():
     build_bytes = (2 * w.indices.numel() + btab.numel() + 2 * T) * 4
     build_ok = bool(torch.equal(b_out, w.indices) and torch.equal(b_lens, w.topk_lens))
     cold_ms = time_cold(step, 10, stream)
+    gathered = int(active_slots_per_token(w).sum()) * ROW_BYTES
+    return {
+        "gather_only_GBps": round(gathered / (sum(gper) / len(gper) * 1e-3) / 1e9, 1),
+        "gather_only_ms": sum(gper) / len(gper),
+        "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
+        "two_segment_GBps": round(gathered / (sum(sper) / len(sper) * 1e-3) / 1e9, 1),
+        "two_segment_vs_combined": round((sum(cper) / len(cper)) / (sum(sper) / len(sper)), 4),
+        "paged_GBps": round(gathered / (sum(pper) / len(pper) * 1e-3) / 1e9, 1),
+        "paged_vs_combined": round((sum(cper2) / len(cper2)) / (sum(pper) / len(pper)), 4),
+        "build_indices": {"us": round(build_ms * 1e3, 2),
+                          "GBps": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
+                          "bytes": build_bytes,
+                          "hbm_frac": round(build_bytes / (build_ms * 1e-3) / 1e9
+                                            / HBM_PEAK_GBPS, 4),
+                          "rebuilds_the_table": build_ok},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--T", type=int, default=512)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="GPU time of back-to-back launches of the same step "
+                         "before each timed region's warmup (0: none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time the headline alone (settled; no after-idle run, "
+                         "side measurements, T sweep, other configurations or "
+                         "measured peaks): a short command to run under a "
+                         "profiler; by default the line carries all of them")
+    ap.add_argument("--only-workload", choices=WORKLOAD_NAMES,
+                    help="time only this other configuration (as the default line "
+                         "does) and print its record instead of the headline "
+                         "line: a short command to run under a kernel tracer")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy three "
+                         "times (known bytes) for counter calibration")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: the decode is measured on one GPU; --gpus {args.gpus} is "
+              "not supported (tokens would shard across GPUs with no exchange, so "
+              "the per-GPU rate is the one-GPU rate)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_mla_decode_gather_amd import lib, workloads as W
+
+    lib.load()
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    if args.only_workload:
+        rec = other_workloads(stream, only=args.only_workload,
+                              settle_ms=args.settle_ms)[args.only_workload]
+        print(json.dumps({"workload": args.only_workload, **rec}), flush=True)
+        return
+    w = W.make_long_context(args.T, "cuda", seed=4000 + args.T)
+    n_act = active_slots_per_token(w)
+    T = w.T
+    out = torch.empty((T, w.H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((T, w.H), dtype=torch.float32, device="cuda")
+    plan = lib.plan_splits(T, w.H, w.K)
+    ws = lib.alloc_workspace(plan, T, w.H)
+
+    def step():
+        lib.decode(w.q, w.swa_pool, w.comp_pool, w.indices, out, out_lse=lse,
+                   topk_lens=w.topk_lens, seq_lens=w.seq_lens, sinks=w.sinks,
+                   bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
+                   lse_scale=w.lse_scale, plan=plan, workspace=ws, stream=stream)
+
+    after_idle = None
+    if not args.headline_only:
+        # the same W + K steps right after an idle, not settled
+        torch.cuda.synchronize()
+        time.sleep(0.05)
+        a_ms, a_per = time_launches(step, args.steps, args.warmup, stream)
+        after_idle = (a_ms, sum(a_per) / len(a_per))
+    total_ms, per = time_settled(step, args.steps, args.warmup, stream, args.settle_ms)
+    if not args.headline_only:
+        side = side_measurements(w, step, plan, ws, out, lse, args, stream)
     ms_step = total_ms / args.steps
     avg_launch_ms = sum(per) / len(per)
     gathered = int(n_act.sum()) * ROW_BYTES
@@ -471,23 +555,26 @@ def main():
         "tflops": round(achieved_tflops, 1),
         "hbm_frac": round(hbm_frac, 4), "mfma_frac": round(mfma_frac, 4),
         "avg_launch_ms": round(avg_launch_ms, 4),
-        "gather_only_GBps": round(gathered / (sum(gper) / len(gper) * 1e-3) / 1e9, 1),
-        "decode_vs_gather_only": round((sum(gper) / len(gper)) / avg_launch_ms, 4),
-        "cold_cache_GBps": round(gathered / (cold_ms * 1e-3) / 1e9, 1),
-        "two_segment_GBps": round(gathered / (sum(sper) / len(sper) * 1e-3) / 1e9, 1),
-        "two_segment_vs_combined": round((sum(cper) / len(cper)) / (sum(sper) / len(sper)), 4),
-        "paged_GBps": round(gathered / (sum(pper) / len(pper) * 1e-3) / 1e9, 1),
-        "paged_vs_combined": round((sum(cper2) / len(cper2)) / (sum(pper) / len(pper)), 4),
+        "settle": {"gpu_ms": args.settle_ms,
+                   "what": "the same step back to back for about this much GPU "
+                           "time before the W warmup steps of every timed region, "
+                           "so that it sees the clock of sustained load and not "
+                           "the power-management transient that follows an idle"},
         "plan": plan.as_dict(),
         "roofline": roofline,
-        "build_indices": {"us": round(build_ms * 1e3, 2),
-                          "GBps": round(build_bytes / (build_ms * 1e-3) / 1e9, 1),
-                          "bytes": build_bytes,
-                          "hbm_frac": round(build_bytes / (build_ms * 1e-3) / 1e9
-                                            / HBM_PEAK_GBPS, 4),
-                          "rebuilds_the_table": build_ok},
     }
+    if after_idle is not None:
+        result["after_idle"] = {
+            "idle_ms": 50, "ms_per_step": round(after_idle[0] / args.steps, 4),
+            "avg_launch_ms": round(after_idle[1], 4),
+            "gathered_GBps": round(gathered / (after_idle[1] * 1e-3) / 1e9, 1),
+            "frac": round(t_roof / (after_idle[1] * 1e-3), 4),
+            "what": "the same W warmup + K timed steps right after a 50 ms idle, "
+                    "not settled"}
     if not args.headline_only:
+        gms_gather = side.pop("gather_only_ms")
+        result.update(side)
+        result["decode_vs_gather_only"] = round(gms_gather / avg_launch_ms, 4)
         sweep = {}
         for t in (1, 4, 8, 16, 64, 256):
             if t > T:
@@ -501,7 +588,7 @@ def main():
                            out_lse=l2, topk_lens=w.topk_lens[:t], sinks=w.sinks,
                            bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale,
                            plan=p, workspace=wsp)   # current stream (graph capture)
-            tot, pl = time_launches(st, 50, 5, stream)
+            tot, pl = time_settled(st, 50, 5, stream, args.settle_ms)
             g = int(n_act[:t].sum()) * ROW_BYTES
             avg = sum(pl) / len(pl)
             sweep[str(t)] = {"tokens_per_s": round(t * 50 / (tot * 1e-3), 1),
@@ -515,8 +602,7 @@ def main():
                 sweep[str(t)]["graph_launch_us"] = round(gms * 1e3, 2)
                 sweep[str(t)]["graph_gathered_GBps"] = round(g / (gms * 1e-3) / 1e9, 1)
         result["sweep"] = sweep
-    if not args.headline_only:
-        result["workloads"] = other_workloads(stream)
+        result["workloads"] = other_workloads(stream, settle_ms=args.settle_ms)
         peaks = measured_peaks(stream)
         roofline["measured_peaks"] = peaks
         t_meas = max(gathered / (peaks["hbm_read_GBps"] * 1e9),

@@ -1,12 +1,16 @@
 """Summaries of rocprofv3 output for the decode kernel (text, for profiles/).
 
-    python -m sparse_mla_decode_gather_amd.rocprof_summary stats <dir> <cmd>
+    python -m sparse_mla_decode_gather_amd.rocprof_summary stats <dir> <cmd> [<K>]
     python -m sparse_mla_decode_gather_amd.rocprof_summary traffic \\
         <fetch_dir> <write_dir> <copy_bytes> <cmd> [<request_dir>]
     python -m sparse_mla_decode_gather_amd.rocprof_summary sq <cmd> <dir>...
 
 ``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv): the
-decode, combine and combined-table builder kernels.
+decode, combine and combined-table builder kernels.  With K it adds, from
+kernel_trace.csv, the duration statistics of the last K dispatches of the
+most-dispatched decode kernel: under ``bench.py --headline-only --steps K``
+those are the K timed launches (its earlier dispatches are the settling
+and warmup launches).
 ``sq`` gives the median per dispatch of every counter in one or more
 --pmc runs over the decode kernels, with the MFMA-busy and waiting
 fractions derived from them.
@@ -63,6 +67,32 @@ def stats(directory: str, cmd: str) -> str:
             lines.append(f"{short} | {r['Calls']} | {float(r['AverageNs']):.0f} | "
                          f"{r['MinNs']} | {r['MaxNs']} | {float(r['Percentage']):.2f}")
     return "\n".join(lines) + "\n"
+
+
+def timed_tail(directory: str, k: int) -> str:
+    """Duration statistics of the last k dispatches (by start time) of the
+    most-dispatched decode kernel in kernel_trace.csv."""
+    rows = [r for r in _csv(directory, "kernel_trace.csv")
+            if any(d in r["Kernel_Name"] for d in DECODE)]
+    if not rows:
+        raise ValueError("no decode kernel dispatches in the trace")
+    counts = {}
+    for r in rows:
+        counts[r["Kernel_Name"]] = counts.get(r["Kernel_Name"], 0) + 1
+    name = max(counts, key=counts.get)
+    mine = sorted((r for r in rows if r["Kernel_Name"] == name),
+                  key=lambda r: int(r["Start_Timestamp"]))
+    if len(mine) < k:
+        raise ValueError(f"{len(mine)} dispatches of the decode kernel, fewer than {k}")
+    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine[-k:]]
+    short = name.replace("smla::(anonymous namespace)::", "")
+    short = short.replace("void ", "").split("(smla::")[0]
+    return (f"# timed region: the last {k} of {len(mine)} dispatches of {short}\n"
+            f"timed_dispatches: {k}\n"
+            f"timed_average_ns: {statistics.fmean(dur):.0f}\n"
+            f"timed_median_ns: {statistics.median(dur):.0f}\n"
+            f"timed_min_ns: {min(dur)}\n"
+            f"timed_max_ns: {max(dur)}\n")
 
 
 def _per_dispatch(rows, counter, pattern_ok):
@@ -173,6 +203,8 @@ if __name__ == "__main__":
     mode = sys.argv[1]
     if mode == "stats":
         print(stats(sys.argv[2], sys.argv[3]), end="")
+        if len(sys.argv) > 4:
+            print(timed_tail(sys.argv[2], int(sys.argv[4])), end="")
     elif mode == "traffic":
         print(traffic(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5],
                       sys.argv[6] if len(sys.argv) > 6 else None), end="")
