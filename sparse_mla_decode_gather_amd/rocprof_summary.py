@@ -8,9 +8,10 @@
 ``stats`` condenses a --kernel-trace --stats run (kernel_stats.csv): the
 decode, combine and combined-table builder kernels.  With K it adds, from
 kernel_trace.csv, the duration statistics of the last K dispatches of the
-most-dispatched decode kernel: under ``bench.py --headline-only --steps K``
-those are the K timed launches (its earlier dispatches are the settling
-and warmup launches).
+most-dispatched decode kernel (and of the combine kernel, if it ran): under
+``bench.py --headline-only --steps K`` those are the K timed launches (the
+earlier dispatches are the settling and warmup launches); under
+``bench.py --only-workload NAME`` the last 100 are its HIP-graph replays.
 ``sq`` gives the median per dispatch of every counter in one or more
 --pmc runs over the decode kernels, with the MFMA-busy and waiting
 fractions derived from them.
@@ -71,28 +72,34 @@ def stats(directory: str, cmd: str) -> str:
 
 def timed_tail(directory: str, k: int) -> str:
     """Duration statistics of the last k dispatches (by start time) of the
-    most-dispatched decode kernel in kernel_trace.csv."""
-    rows = [r for r in _csv(directory, "kernel_trace.csv")
-            if any(d in r["Kernel_Name"] for d in DECODE)]
-    if not rows:
+    most-dispatched decode kernel in kernel_trace.csv, and of the combine
+    kernel's last k when it ran."""
+    rows = _csv(directory, "kernel_trace.csv")
+    dec = [r for r in rows if any(d in r["Kernel_Name"] for d in DECODE)]
+    if not dec:
         raise ValueError("no decode kernel dispatches in the trace")
     counts = {}
-    for r in rows:
+    for r in dec:
         counts[r["Kernel_Name"]] = counts.get(r["Kernel_Name"], 0) + 1
-    name = max(counts, key=counts.get)
-    mine = sorted((r for r in rows if r["Kernel_Name"] == name),
-                  key=lambda r: int(r["Start_Timestamp"]))
-    if len(mine) < k:
-        raise ValueError(f"{len(mine)} dispatches of the decode kernel, fewer than {k}")
-    dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine[-k:]]
-    short = name.replace("smla::(anonymous namespace)::", "")
-    short = short.replace("void ", "").split("(smla::")[0]
-    return (f"# timed region: the last {k} of {len(mine)} dispatches of {short}\n"
-            f"timed_dispatches: {k}\n"
-            f"timed_average_ns: {statistics.fmean(dur):.0f}\n"
-            f"timed_median_ns: {statistics.median(dur):.0f}\n"
-            f"timed_min_ns: {min(dur)}\n"
-            f"timed_max_ns: {max(dur)}\n")
+    names = [max(counts, key=counts.get)]
+    names += sorted({r["Kernel_Name"] for r in rows if "combine_kernel" in r["Kernel_Name"]})
+    out = []
+    for name in names:
+        mine = sorted((r for r in rows if r["Kernel_Name"] == name),
+                      key=lambda r: int(r["Start_Timestamp"]))
+        if len(mine) < k:
+            raise ValueError(f"{len(mine)} dispatches of {name}, fewer than {k}")
+        dur = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in mine[-k:]]
+        short = name.replace("smla::(anonymous namespace)::", "")
+        short = short.replace("void ", "").split("(smla::")[0]
+        tag = "combine_" if "combine_kernel" in name else ""
+        out += [f"# the last {k} of {len(mine)} dispatches of {short}",
+                f"{tag}tail_dispatches: {k}",
+                f"{tag}tail_average_ns: {statistics.fmean(dur):.0f}",
+                f"{tag}tail_median_ns: {statistics.median(dur):.0f}",
+                f"{tag}tail_min_ns: {min(dur)}",
+                f"{tag}tail_max_ns: {max(dur)}"]
+    return "\n".join(out) + "\n"
 
 
 def _per_dispatch(rows, counter, pattern_ok):
