@@ -294,10 +294,14 @@ __device__ __forceinline__ u32x4 packed_load_row(const uint8_t* row, const Packe
   return u32x4{a[0], a[1], b[0], b[1]};
 }
 
-// UE8M0 scale byte -> the binary32 power of two 2^(e - 127) (e = 255: NaN).
+// UE8M0 scale byte e -> the scale operand of the scaled FP8 conversion.  The
+// conversion reads only the exponent field of that operand, as an E8M0
+// value (measured on gfx950: field 0 scales by 2^-127, field 255 gives NaN,
+// as UE8M0 defines them), so the bits e << 23 are the whole decode; as a
+// binary32 they would be 0 for e = 0 and +inf for e = 255, which is why the
+// operand is not used as a number anywhere else.
 __device__ __forceinline__ float ue8m0_scale(uint32_t e) {
-  const uint32_t bits = e == 0u ? 0x00400000u : (e == 255u ? 0x7FC00000u : e << 23);
-  return __uint_as_float(bits);
+  return __uint_as_float(e << 23);
 }
 
 // 8 E4M3FN codes times a power-of-two scale -> 8 BF16 values (exact for

@@ -5,7 +5,8 @@ against the oracle's decode of the same bytes.
   is exactly a BF16 row, so the GPU result must equal it bit for bit --
   this pins the byte layout, the per-block scale selection and the RoPE
   lanes' stores of the kernels, for both head counts, split and unsplit, at
-  the first and last rows of both pools and for scale bytes far from 127.
+  the first and last rows of both pools, for scale bytes far from 127 and
+  for scale bytes at both ends of the UE8M0 range (0..2, 252..254).
 * Element-wise parity (the FP8 bar, 3e-2 + 3e-2*|ref|, LSE 1e-3) with
   ragged lengths, -1 slots, several table segments, padded rows, the
   two-segment and page-table forms, and every token of the full-size
@@ -80,6 +81,56 @@ def test_single_slot_is_the_decoded_row_bit_for_bit(H):
         assert np.all(lse.cpu().numpy() == 0.0), (H, S)
         ref = oracle_for(w, range(T))
         compare(out, lse, ref, TOL_FP8, what=f"packed single slot H={H} S={S}")
+
+
+def edge_scale_rows(seed):
+    """Rows whose scale bytes sit at the ends of the UE8M0 range, with codes
+    that keep every decoded value a normal BF16 number: scale bytes 0..2
+    (2^-127..2^-125) with codes of magnitude >= 2 (E4M3FN exponent field >=
+    8) and scale bytes 252..254 with codes below 2 (field <= 7), one row of
+    each kind and one alternating them block by block."""
+    rng = np.random.default_rng(seed)
+    rows = W.packed_rows(3, seed, "cpu").numpy().copy()
+
+    def codes(n, big):
+        ex = rng.integers(8, 16, n) if big else rng.integers(0, 8, n)
+        man = rng.integers(0, 8, n)
+        man = np.where((ex == 15) & (man == 7), 6, man)      # 0x7F / 0xFF are NaN
+        return ((rng.integers(0, 2, n) << 7) | (ex << 3) | man).astype(np.uint8)
+    lows, highs = rng.integers(0, 3, 8), rng.integers(252, 255, 8)
+    for r, kinds in enumerate(([True] * 8, [False] * 8, [j % 2 == 0 for j in range(8)])):
+        for j, big in enumerate(kinds):
+            rows[r, 56 * j:56 * j + 56] = codes(56, big)
+            rows[r, 576 + j] = lows[j] if big else highs[j]
+    return torch.from_numpy(rows)
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_scale_bytes_at_the_range_ends_decode_exactly(H):
+    """UE8M0 bytes 0..2 and 252..254 (reading S20: 2^(e-127)): the single
+    active slot returns the decoded row bit for bit, so byte 0 scales by
+    2^-127 (not 0) and byte 254 by 2^127."""
+    need_gpu()
+    rows = edge_scale_rows(31)
+    want = oracle.packed584_to_f64(W.raw_bits(rows))
+    assert np.all(np.isfinite(want)) and np.array_equal(oracle.round_to_bf16(want), want)
+    assert np.all(np.abs(want[:, :448][want[:, :448] != 0]) >= 2.0 ** -126)
+    swa = rows.cuda()
+    comp = rows.flip(0).contiguous().cuda()
+    T, K = 6, 160
+    idx = np.full((T, K), -1, np.int32)
+    picks = [(0, 0), (5, 1), (127, 2), (128, 2), (140, 1), (159, 0)]   # (col, pool row)
+    for t, (c, r) in enumerate(picks):
+        idx[t, c] = r
+    w = wl(idx, H=H, swa=swa, comp=comp, sinks=False, q_zero=True)
+    expect = [want[r] if c < 128 else want[2 - r] for c, r in picks]
+    for S in (1, 2):
+        log(f"[packed] scale-byte ends H={H} S={S}")
+        out, lse = run_decode(w, plan=L.plan_splits(T, H, K, L.DTYPE_BF16, PK, num_splits=S))
+        o = out.float().cpu().numpy()
+        for t in range(T):
+            assert np.array_equal(o[t], np.tile(expect[t], (H, 1))), (H, S, t)
+        assert np.all(lse.cpu().numpy() == 0.0), (H, S)
 
 
 @pytest.mark.parametrize("H", [64, 128])
