@@ -19,8 +19,9 @@
 //    and out-of-range slots are dropped), so tiles are dense.
 //  * Rows are gathered 32 at a time into row-major LDS tiles with a padded
 //    pitch (conflict-free row and transposed reads), by LDS-DMA for BF16
-//    rows and through registers for FP8 rows (widened to BF16 on the way;
-//    every E4M3FN value is exactly a BF16 value).
+//    rows and through registers for FP8 rows and packed block-scaled rows
+//    (widened to BF16 on the way; every E4M3FN value, and every E4M3FN value
+//    times a power of two in BF16's normal range, is exactly a BF16 value).
 //  * S^T = K Q^T on MFMA 32x32x16 BF16 (A = tile rows from LDS, B = 32
 //    heads of Q held in registers).  The accumulator layout of S^T is the
 //    B-operand layout P^T needs for O^T = V^T P^T, so probabilities go to
@@ -30,11 +31,11 @@
 //    first tile and left alone; a tile exceeding it by more than 2^64 makes
 //    the split start over with the higher reference, so O is never rescaled
 //    and the result is exact up to rounding.
-//  * decode_kernel (H=64, BF16 or FP8 rows): wave w computes S and O for
-//    its own 32 heads.  decode_hd_kernel (H=128, BF16 or FP8 rows): wave w
-//    computes S for 32 heads but O for a quarter of the output dims of all
-//    heads, with P exchanged through LDS (see there).  FP8 q and FP8 rows
-//    are widened exactly to BF16 and multiplied on the BF16 MFMA.
+//  * decode_kernel (H=64): wave w computes S and O for its own 32 heads.
+//    decode_hd_kernel (H=128): wave w computes S for 32 heads but O for a
+//    quarter of the output dims of all heads, with P exchanged through LDS
+//    (see there).  FP8 q and FP8 rows are widened exactly to BF16 and
+//    multiplied on the BF16 MFMA.
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
 //    merges them.

@@ -19,8 +19,9 @@ fractions derived from them.
 into HBM bytes per decode launch, calibrated by the same counters on a
 plain device copy of known size taken in the same process: the factor is
 counter bytes / true bytes of the copy, and decode traffic = counter
-bytes / factor.  The result is tagged with a digest of the kernel sources,
-so a stale figure is ignored once the kernel changes.  With a third run of
+bytes / factor.  The result is tagged with a digest of the kernel sources
+as code (comments and layout excluded), so a stale figure is ignored once
+the kernel code changes.  With a third run of
 the EA read-request counters by size (TCC_EA0_RDREQ_sum, _128B_sum,
 _32B_sum) the summary adds an uncalibrated cross-check of the read bytes.
 """
@@ -39,11 +40,40 @@ DECODE = ("decode_kernel", "decode_hd_kernel")   # the decode kernels (not gathe
 COPY_PATTERNS = ("copy", "Copy")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed
+    (string and character literals kept as written), so that an edit of a
+    comment or of the layout does not count as a change of the kernels."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest() -> str:
+    """Digest of the kernel and host-layer sources as code (comments and
+    layout excluded): a traffic figure is only used on the code it was
+    measured on."""
     h = hashlib.sha256()
     for f in ("kernels.hip", "api.cpp", "internal.h"):
-        with open(os.path.join(PKG, "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(PKG, "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -129,3 +129,12 @@ def test_bench_uses_traffic_only_on_the_current_source(tmp_path):
     assert bench.measured_traffic() is None
     bench.COUNTERS = str(tmp_path / "missing.txt")
     assert bench.measured_traffic() is None
+
+
+def test_digest_ignores_comments_and_layout():
+    code = 'int a = 1;\nfloat b = a * 2;  // scale\nconst char* s = "x // y";\n'
+    same = '/* header */\nint a = 1;   float b = a * 2;\nconst char* s = "x // y";  // s\n'
+    other = 'int a = 1;\nfloat b = a * 3;\nconst char* s = "x // y";\n'
+    assert rs._code_only(code) == rs._code_only(same)
+    assert rs._code_only(code) != rs._code_only(other)
+    assert '"x // y"' in rs._code_only(code)
