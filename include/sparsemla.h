@@ -93,6 +93,17 @@ typedef struct ihipStream_t* smla_stream_t;
  * sparse_mla_get_device_error.  Violating slots are skipped either way:
  * an out-of-range index is never dereferenced, with or without the flag. */
 #define SMLA_FLAG_VALIDATE_INDICES 1u
+/* A check for races in the kernels' tile pipeline, not a production path:
+ * every step of the pipeline (the row loads of a tile, the S^T products, the
+ * O^T products and softmax) completes, and all waves of the workgroup meet,
+ * before the next step starts.  The arithmetic is unchanged, so the results
+ * must be bitwise identical to the same call without the flag; a difference
+ * means that overlapping steps disturbed each other.  Slower.  Combined-table
+ * calls only (sparse_mla_decode, sparse_mla_decode_noalloc); with the
+ * two-segment or page-table forms, or sparse_mla_gather_only, the call
+ * returns SMLA_ERR_INVALID_ARG.  Any flag bit not defined here is
+ * SMLA_ERR_INVALID_ARG too. */
+#define SMLA_FLAG_SERIAL_PIPELINE 2u
 
 /* Device-side error codes reported by sparse_mla_get_device_error. */
 #define SMLA_DEVERR_NONE          0

@@ -194,6 +194,11 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
                  bool with_outputs, smla::DecodeParams* p, Layout* L) {
   if (!a) return SMLA_ERR_INVALID_ARG;
   if (a->T < 0 || a->K < 1) return SMLA_ERR_INVALID_ARG;
+  if ((uint32_t)a->flags & ~(SMLA_FLAG_VALIDATE_INDICES | SMLA_FLAG_SERIAL_PIPELINE))
+    return SMLA_ERR_INVALID_ARG;
+  // the serialized pipeline is built for the combined table and the decode
+  const bool serial = (a->flags & SMLA_FLAG_SERIAL_PIPELINE) != 0;
+  if (serial && (seg || pg || !with_outputs)) return SMLA_ERR_INVALID_ARG;
   if (a->H != 64 && a->H != 128) return SMLA_ERR_UNSUPPORTED_SHAPE;
   if (!dtype_pair_ok(a->q_dtype, a->kv_dtype)) return SMLA_ERR_UNSUPPORTED_DTYPE;
   if (with_outputs && !scales_ok(a->bmm1_scale, a->bmm2_scale, a->lse_scale))
@@ -320,6 +325,7 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
     int cus = 0;
     p->rank_items = (query_cu_count(&cus) != SMLA_OK || (int64_t)a->T * S > cus) ? 1 : 0;
   }
+  p->serial = serial ? 1 : 0;
   if (with_outputs && S > 1) {
     p->mid_lse = reinterpret_cast<float*>(ws + L->mid_lse);
     p->mid_out = reinterpret_cast<uint16_t*>(ws + L->mid_out);

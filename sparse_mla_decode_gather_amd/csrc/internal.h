@@ -58,6 +58,9 @@ struct DecodeParams {
   // H=128 kernel: start the items of an XCD longest first (set when the
   // grid has more items than the device has compute units)
   int32_t rank_items;
+  // launch the serialized tile pipeline (SMLA_FLAG_SERIAL_PIPELINE: an
+  // LDS-race check, combined table only); read by the host dispatch
+  int32_t serial;
 };
 
 struct CombineParams {

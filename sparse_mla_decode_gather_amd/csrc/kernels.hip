@@ -458,10 +458,23 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
   return 8 * (i >> 2) + 4 * kg + (i & 3);
 }
 
-template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false>
+// SERIAL (a check for LDS races, not a production path): every step of the
+// tile pipeline completes, row loads included, and all waves meet at a
+// barrier before the next step starts, so no two steps overlap.  The
+// arithmetic is the same instruction for instruction, so a pipelined call
+// must give the same bits; a difference exposes a race between the steps.
+template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false,
+          bool SERIAL = false>
 __global__ __launch_bounds__(NW * 64, 1)
 void decode_kernel(DecodeParams p) {
   static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
+  // all loads of the wave landed and every wave arrived (SERIAL only)
+  auto serial_point = [](bool wait_loads) {
+    if constexpr (SERIAL) {
+      if (wait_loads) wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
   constexpr int H = NW * 32;              // one wave per 32 heads
   constexpr int NT = NW * 64;
   constexpr int RPW = kTile / NW;         // tile rows each wave gathers
@@ -742,7 +755,8 @@ void decode_kernel(DecodeParams p) {
       // whole) are a compile-time variant with no branches in their body.
       auto iteration = [&](auto steady, int it) {
         constexpr bool kSteady = decltype(steady)::value;
-        wait_tile(it, min(it + NSTAGE - 2, ntiles - 1));
+        if constexpr (SERIAL) wait_vmcnt<0>();
+        else wait_tile(it, min(it + NSTAGE - 2, ntiles - 1));
         __syncthreads();            // every wave's rows landed; tile it-1 done
         // The rows of tile it+NSTAGE-1 go out while the S^T MFMAs of tile
         // it run (RPW rows, spread over the 32 MFMAs).
@@ -756,9 +770,11 @@ void decode_kernel(DecodeParams p) {
           for (int r = 0; r < RPW / 8; ++r)
             if (do_issue) issue_row(nxt, q * (RPW / 8) + r, codes);
         });
+        serial_point(true);
         bf16x8 pf[2];
         softmax(sv, n_in(it), pf, steady);
         pv(stage(it), pf, pv_no_hook);
+        serial_point(false);
       };
       int it = 0;
       for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
@@ -831,6 +847,7 @@ void decode_kernel(DecodeParams p) {
           for (int r = 0; r < RPW / 8; ++r)
             if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
         });
+        serial_point(true);
         bf16x8 pf[2];
         softmax(sv, n_in(it), pf, steady);
         if constexpr (kSteady) {
@@ -845,6 +862,7 @@ void decode_kernel(DecodeParams p) {
           pv(stage(it), pf, pv_no_hook);
           if (do_load) store(nxt);
         }
+        serial_point(false);
       };
       int it = 0;
       for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
@@ -934,10 +952,17 @@ void decode_kernel(DecodeParams p) {
 // BF16 rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
+// SERIAL: the LDS-race check of decode_kernel (see there) for this kernel.
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false,
-          bool STREAM = false, bool PACKED = false>
+          bool STREAM = false, bool PACKED = false, bool SERIAL = false>
 __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
+  auto serial_point = [](bool wait_loads) {
+    if constexpr (SERIAL) {
+      if (wait_loads) wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
   constexpr int NW = 4, H = 128, NT = 256;
   constexpr int RPW = kTile / NW;         // rows each wave gathers per tile
   // LDS tiles: i-1 (read by O^T), i (S^T), i+1 and i+2 (landing).
@@ -1400,6 +1425,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
             for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
             if constexpr (decltype(pv)::value) pv_prefetch(vt, pr, pfr, vfr);
           }
+          serial_point(true);
           // the row addresses of tile it+3 (those of tile it+2 were used by
           // the loads above): slot code under the first MFMAs, readouts
           // between the last ones, which have no softmax work beside them
@@ -1412,6 +1438,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
               if (k >= 24 && k < 24 + RPW) rows[k - 24] = row_of_lane(addr, k - 24);
             }
           });
+          serial_point(false);
         };
         using T_ = BoolC<true>;
         using F_ = BoolC<false>;
@@ -1456,7 +1483,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       // also orders P^T of tile it-1 before its readers and frees the stage
       // of tile it-2 for tile it+2.
       auto land = [&](int it) {
-        if (it + 1 < ntiles) wait_vmcnt<RPW>();
+        if (!SERIAL && it + 1 < ntiles) wait_vmcnt<RPW>();
         else wait_vmcnt<0>();
         __syncthreads();
       };
@@ -1465,9 +1492,11 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         const bool di = 2 < ntiles;
         bf16x8 pfr[NHB], vfr[kVLead];
         const f32x16 sv0 = qk_tile(0, di);
+        serial_point(true);
         if constexpr (!GATHER_ONLY)
           step_block(BoolC<false>{}, kv_lds, p_lds, pfr, vfr, sv0, p_lds, no_hook);
         if (di) fetch_rows(min(3, ntiles - 1), rows);
+        serial_point(false);
       }
       // Iteration it: land tile it, O^T of tile it-1 with the S^T and
       // softmax of tile it, the rows of tile it+2 issued during S^T.  STEADY
@@ -1476,7 +1505,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
       auto iteration = [&](auto steady, int it) {
         constexpr bool kSteady = decltype(steady)::value && !GATHER_ONLY;
         if constexpr (kSteady) {
-          wait_vmcnt<RPW>();
+          if constexpr (SERIAL) wait_vmcnt<0>();
+          else wait_vmcnt<RPW>();
           __syncthreads();
         } else {
           if (it < ntiles) land(it);
@@ -1509,6 +1539,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;   // no tile: P = 0
         }
+        serial_point(true);
         if constexpr (kSteady) {
           // The rows of tile it+3 (their addresses are no longer needed for
           // tile it+2, whose loads went out above): the slot code is read
@@ -1528,6 +1559,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
                        p_lds + (it & 1) * kPBuf, no_hook);
           if (di) fetch_rows(min(it + 3, ntiles - 1), rows);
         }
+        serial_point(false);
       };
       int it = 1;
       for (; it + 2 < ntiles; ++it) iteration(BoolC<true>{}, it);
@@ -1626,10 +1658,11 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 }
 
-template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM, bool PACKED = false>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM, bool PACKED = false,
+          bool SERIAL = false>
 __global__ __launch_bounds__(256, 1)
 void decode_hd_kernel(DecodeParams p) {
-  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN, STREAM, PACKED>(p);
+  decode_hd_body<Q_FP8, KV_FP8, SPLIT, false, GEN, STREAM, PACKED, SERIAL>(p);
 }
 
 // The row gather of decode_hd_kernel alone (BF16 rows), under its own name.
@@ -1803,6 +1836,16 @@ template <bool QF, bool KF, bool STREAM>
 hipError_t launch_decode_hd_s(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const bool gen = p.segmented != 0;
+  if (p.serial) {            // combined table only (checked on the host)
+    if (gen) return hipErrorInvalidValue;
+    if (p.S > 1)
+      hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, false, false, false, true>), grid,
+                         dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_hd_kernel<QF, KF, false, false, false, false, true>), grid,
+                         dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.S > 1 && gen)
     hipLaunchKernelGGL((decode_hd_kernel<QF, KF, true, true, STREAM>), grid, dim3(256), 0, stream, p);
   else if (p.S > 1)
@@ -1818,7 +1861,7 @@ hipError_t launch_decode_hd_s(const DecodeParams& p, hipStream_t stream) {
 template <bool QF, bool KF>
 hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
   if constexpr (!KF) {
-    if (streaming_rows(p)) return launch_decode_hd_s<QF, KF, true>(p, stream);
+    if (streaming_rows(p) && !p.serial) return launch_decode_hd_s<QF, KF, true>(p, stream);
   }
   return launch_decode_hd_s<QF, KF, false>(p, stream);
 }
@@ -1827,6 +1870,16 @@ hipError_t launch_decode_hd(const DecodeParams& p, hipStream_t stream) {
 hipError_t launch_decode_hd_packed(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const bool gen = p.segmented != 0;
+  if (p.serial) {
+    if (gen) return hipErrorInvalidValue;
+    if (p.S > 1)
+      hipLaunchKernelGGL((decode_hd_kernel<false, true, true, false, false, true, true>), grid,
+                         dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_hd_kernel<false, true, false, false, false, true, true>), grid,
+                         dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
   if (p.S > 1 && gen)
     hipLaunchKernelGGL((decode_hd_kernel<false, true, true, true, false, true>), grid, dim3(256), 0, stream, p);
   else if (p.S > 1)
@@ -1843,6 +1896,16 @@ hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const dim3 block(NW * 64);
   const bool gen = p.segmented != 0;
+  if (p.serial) {
+    if (gen) return hipErrorInvalidValue;
+    if (p.S > 1)
+      hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false, PK, true>), grid, block, 0,
+                         stream, p);
+    else
+      hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false, PK, true>), grid, block, 0,
+                         stream, p);
+    return hipGetLastError();
+  }
   if (p.S > 1 && gen)
     hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, true, PK>), grid, block, 0, stream, p);
   else if (p.S > 1)

@@ -30,6 +30,7 @@ DTYPE_FP8_E4M3FN = 1
 DTYPE_PACKED_FP8_584 = 2        # uint8 pools of 584-byte packed rows
 PACKED_ROW_BYTES = 584
 FLAG_VALIDATE_INDICES = 1
+FLAG_SERIAL_PIPELINE = 2        # LDS-race check: the serialized tile pipeline
 DEVERR = {0: "none", 1: "index out of range", 2: "topk_len out of range"}
 
 

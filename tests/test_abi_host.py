@@ -604,3 +604,29 @@ def test_build_rejects(so, change, code):
     elif change == "misaligned_req":
         b.token_to_req = DUMMY + 3
     assert so.sparse_mla_build_indices(ctypes.byref(b), None) == code
+
+
+# ---------------------------------------------------------------------------
+# flags
+# ---------------------------------------------------------------------------
+
+def test_flags_unknown_bits_and_serial_pipeline_forms(so):
+    """Flag bits other than the defined ones are rejected; the serialized
+    tile pipeline (an LDS-race check) is offered on the combined-table
+    decode only, not with the two-segment or page-table forms or the
+    gather-only call."""
+    a = good_args()
+    a.flags = 4
+    assert call(so, a) == 1
+    a.flags = L.FLAG_SERIAL_PIPELINE | L.FLAG_VALIDATE_INDICES
+    assert call(so, a, bad_plan(a)) == 6          # every argument check passed
+    s, g = seg_args(), good_segments()
+    s.flags = L.FLAG_SERIAL_PIPELINE
+    assert call_seg(so, s, g, bad_plan(s)) == 1
+    pa, pg = paged_args(), good_paged(128, 30, 64)
+    pa.topk_lens = DUMMY
+    pa.flags = L.FLAG_SERIAL_PIPELINE
+    assert call_paged(so, pa, pg, bad_plan(pa)) == 1
+    ga = good_args()
+    ga.flags = L.FLAG_SERIAL_PIPELINE
+    assert call_gather(so, ga) == 1
