@@ -20,11 +20,13 @@ namespace {
 constexpr int kDefaultMaxSplits = 16;   // FlashInfer cake_* default max_splits
 constexpr int kChunkCols = 64;          // split granularity in table columns
 
-// Cost model constants, in units of "one gathered 1 KB row" of one
-// workgroup's time: fixed per-workgroup cost (Q load, compaction,
-// epilogue) and the combine launch.
+// Cost model constants, in units of "one gathered row" of one workgroup's
+// time: fixed per-workgroup cost (Q load, compaction, epilogue), the
+// combine launch, and what each further split adds to the combine (one more
+// partial row to fetch and merge per output row).
 constexpr int64_t kWgOverheadRows = 96;
 constexpr int64_t kCombineLaunchRows = 32;
+constexpr int64_t kPerSplitRows = 8;
 
 std::mutex g_cu_mutex;
 int g_cu_count[64] = {0};
@@ -128,9 +130,12 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     // Workgroups resident per CU: one at H=128 (it holds 32 heads of O per
     // wave in registers), two at H=64.
     const int64_t slots = (int64_t)num_cus * (H == 64 ? 2 : 1);
-    // Per-row cost relative to a BF16 row: FP8 rows (512 B) and packed rows
-    // (584 B) move about half the bytes.
-    const int64_t row_w = (kv_dtype == SMLA_DTYPE_BF16) ? 2 : 1;
+    // Per-row cost: the same for every row format.  Rows are widened to BF16
+    // and multiplied on the BF16 MFMA, whose work per row is the same, so
+    // the row count and not its bytes sets a split's time (weighting FP8
+    // rows by their half-size bytes picked one split where 4-8 ran up to
+    // 1.5x faster: H=128 FP8 rows, K=512, T=16-48).
+    const int64_t row_w = 2;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {
       const int64_t cps = (num_chunks + s - 1) / s;
@@ -141,7 +146,7 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
                              (s > 1 ? 2 * (int64_t)H : 0);
       int64_t cost = waves * per_wg;
       if (s > 1)
-        cost += 2 * kCombineLaunchRows +
+        cost += 2 * kCombineLaunchRows + kPerSplitRows * s +
                 (2 * (int64_t)T * H * s + num_cus - 1) / num_cus;
       if (cost < best) {
         best = cost;
