@@ -20,13 +20,15 @@ namespace {
 constexpr int kDefaultMaxSplits = 16;   // FlashInfer cake_* default max_splits
 constexpr int kChunkCols = 64;          // split granularity in table columns
 
-// Cost model constants, in units of "one gathered row" of one workgroup's
-// time: fixed per-workgroup cost (Q load, compaction, epilogue), the
-// combine launch, and what each further split adds to the combine (one more
-// partial row to fetch and merge per output row).
+// Cost model, in units of half a gathered row of one workgroup's time (a
+// row costs 2): a fixed cost per workgroup (Q load, compaction, epilogue),
+// a split's partial write (kPartialPerHead per head), and the combine's
+// reads of every partial row, spread over the CUs (kCombinePerRow per
+// partial row).  The constants were fitted to forced-split timings over
+// H = 64 / 128, BF16 and FP8 rows, K = 512 .. 2048 and T = 1 .. 192.
 constexpr int64_t kWgOverheadRows = 96;
-constexpr int64_t kCombineLaunchRows = 32;
-constexpr int64_t kPerSplitRows = 8;
+constexpr int64_t kPartialPerHead = 1;
+constexpr int64_t kCombinePerRow = 4;
 
 std::mutex g_cu_mutex;
 int g_cu_count[64] = {0};
@@ -141,13 +143,11 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
       const int64_t cps = (num_chunks + s - 1) / s;
       const int64_t rows = std::min<int64_t>(cps * kChunkCols, K);
       const int64_t waves = ((int64_t)T * s + slots - 1) / slots;
-      // a split writes a BF16 partial of H rows-worth of bytes
       const int64_t per_wg = 2 * kWgOverheadRows + rows * row_w +
-                             (s > 1 ? 2 * (int64_t)H : 0);
+                             (s > 1 ? kPartialPerHead * (int64_t)H : 0);
       int64_t cost = waves * per_wg;
       if (s > 1)
-        cost += 2 * kCombineLaunchRows + kPerSplitRows * s +
-                (2 * (int64_t)T * H * s + num_cus - 1) / num_cus;
+        cost += (kCombinePerRow * (int64_t)T * H * s + num_cus - 1) / num_cus;
       if (cost < best) {
         best = cost;
         S = s;
