@@ -187,10 +187,14 @@ typedef struct smla_decode_args {
  *   forces S = clamp(override, 1, min(num_chunks, SMLA_MAX_SPLITS));
  *   num_cus <= 0 queries the current device's compute-unit count once and
  *   caches it per device.
+ *   The dtypes are checked but do not change the plan: every row format is
+ *   widened and multiplied on the BF16 MFMA, so a split's time follows its
+ *   row count.
  * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1, K > SMLA_MAX_PLAN_COLUMNS
  * or a NULL out_plan,
- * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128}, SMLA_ERR_HIP if the
- * device query fails. */
+ * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128},
+ * SMLA_ERR_UNSUPPORTED_DTYPE for a (q, kv) pair the decode does not take,
+ * SMLA_ERR_HIP if the device query fails. */
 int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
                            int max_splits, int num_splits_override,
                            int num_cus, smla_plan* out_plan);
