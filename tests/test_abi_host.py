@@ -630,3 +630,21 @@ def test_flags_unknown_bits_and_serial_pipeline_forms(so):
     ga = good_args()
     ga.flags = L.FLAG_SERIAL_PIPELINE
     assert call_gather(so, ga) == 1
+
+
+@pytest.mark.parametrize("T,H,K,kv,S", [
+    (4, 64, 256, 0, 4),        # tiny
+    (64, 128, 512, 0, 2),      # batched with sinks
+    (128, 64, 1024, 1, 4),     # FP8 q and rows
+    (1, 128, 2048, 0, 16), (4, 128, 2048, 0, 16), (8, 128, 2048, 0, 16),
+    (16, 128, 2048, 0, 11), (32, 128, 2048, 0, 8), (64, 128, 2048, 0, 4),
+    (128, 128, 2048, 0, 2), (512, 128, 2048, 0, 1),
+    (512, 128, 2048, 1, 1),    # speculative decode (FP8 rows, BF16 q)
+    (16, 128, 512, 1, 4),      # FP8 rows plan by row count, not bytes (was 1)
+])
+def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S):
+    """The planner's picks for the benchmarked shapes on a 256-CU device
+    (each the fastest or within ~2% of the fastest forced split measured on
+    MI355X; the cost model is deterministic, so these are exact)."""
+    q = 1 if (kv == 1 and H == 64) else 0
+    assert plan(T, H, K, q=q, kv=kv, cus=256).num_splits == S
