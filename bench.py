@@ -35,7 +35,7 @@ launches evicts L2 and MALL), the per-T numbers for T in 1, 4, 8, 16, 64,
 the other configurations (tiny, batched with sinks, FP8, speculative
 decode, and the long-context shape with packed 584-byte block-scaled FP8
 rows) with their default plans and roofline fractions, and the roofline
-fraction against peaks measured on the box.
+fraction against peaks measured on the same device in the same run.
 
 Prints ONE JSON line.  Options: --steps, --warmup, --gpus (1 only), --T,
 --settle-ms, --no-cpu-baseline, --headline-only (the headline's settled
@@ -244,7 +244,7 @@ def cpu_baseline(w, budget_s=10.0):
 
 
 def measured_peaks(stream):
-    """Attainable peaks on this machine, for the fractions against measured
+    """Attainable peaks of this device, for the fractions against measured
     rather than published peaks: streaming HBM rates of library kernels
     (torch's sum and row sums over 4 GiB, one read pass each, and a 2 GiB
     copy counted as read + write) and dense BF16 GEMMs of 8192^3 on N(0,1)
