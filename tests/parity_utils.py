@@ -38,8 +38,13 @@ def host_case(w: W.Workload, tokens):
         ok = (part >= 0) & (part < (0 if pool is None else pool.shape[0]))
         uniq = np.unique(part[ok])
         if pool is None or len(uniq) == 0:
-            dt = torch.bfloat16 if pool is None else pool.dtype
-            pools.append(W.raw_bits(torch.zeros((1, 512), dtype=dt)))
+            # a stand-in row in the workload's row format (never indexed)
+            if w.kv_dtype == W.PACKED:
+                dt, width = torch.uint8, W.PACKED_ROW_BYTES
+            else:
+                dt, width = (torch.bfloat16 if w.kv_dtype == W.BF16
+                             else torch.float8_e4m3fn), 512
+            pools.append(W.raw_bits(torch.zeros((1, width), dtype=dt)))
             continue
         rows = pool[torch.as_tensor(uniq, device=pool.device)]
         pools.append(W.raw_bits(rows))
