@@ -157,3 +157,26 @@ def test_paged_validate_reports_pages_and_lengths():
     c["tot"][3] = 49                        # beyond window + every slot
     run(c, plan, L.FLAG_VALIDATE_INDICES, ws)
     assert L.get_device_error(ws)[:2] == (2, 3)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_paged_shapes_match_oracle(seed):
+    """Seeded random page-table calls: window widths 0..128, 0..20 pages of
+    1..96 rows, both head counts and format pairs, lengths, sinks, planner,
+    unsplit or random split counts."""
+    need_gpu()
+    rng = np.random.default_rng(9000 + seed)
+    K1 = int(rng.integers(0, 129))
+    ps = int(rng.choice([1, 16, 37, 64, 96]))
+    pages = int(rng.integers(0 if K1 else 1, 21))
+    H = int(rng.choice([64, 128]))
+    q, kv = [(W.BF16, W.BF16), (W.BF16, W.FP8), (W.FP8, W.FP8)][int(rng.integers(3))]
+    T = int(rng.integers(1, 7))
+    c = make(T, K1, pages, ps, H=H, kv=kv, q=q, seed=9000 + seed,
+             swa_rows=int(rng.integers(1, 700)), n_pages=max(pages, int(rng.integers(1, 120))),
+             lens=bool(rng.random() < 0.7), sinks=bool(rng.random() < 0.5))
+    K = K1 + pages * ps
+    S = int(rng.choice([0, 1, int(rng.integers(1, -(-K // 64) + 1))]))
+    plan = L.plan_splits(T, H, K, L.dtype_code(c["q"]), L.dtype_code(c["swa"]), num_splits=S)
+    check(c, f"random seed={seed} K1={K1} pages={pages}x{ps} H={H} q={q} kv={kv} "
+             f"S={plan.num_splits}", plan=plan)

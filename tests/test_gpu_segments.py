@@ -188,3 +188,26 @@ def test_ragged_segments_batch_order_does_not_change_any_token():
         b, lb = run(cp, plan=plan)
         same_bits(a[perm], b, str(S))
         assert torch.equal(la[perm], lb), S
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_segment_shapes_match_oracle(seed):
+    """Seeded random two-segment calls: widths 0..300 / 0..1200 (not both
+    0), both head counts and format pairs, -1 densities, lengths, sinks,
+    planner, unsplit or random split counts."""
+    need_gpu()
+    rng = np.random.default_rng(7000 + seed)
+    K1 = int(rng.choice([0, int(rng.integers(1, 300))]))
+    K2 = int(rng.integers(0 if K1 else 1, 1200))
+    H = int(rng.choice([64, 128]))
+    q, kv = [(W.BF16, W.BF16), (W.BF16, W.FP8), (W.FP8, W.FP8)][int(rng.integers(3))]
+    T = int(rng.integers(1, 7))
+    c = make(T, K1, K2, H=H, kv=kv, q=q, seed=7000 + seed,
+             neg=float(rng.choice([0.0, 0.1, 0.6])), lens=bool(rng.random() < 0.7),
+             sinks=bool(rng.random() < 0.5), swa_rows=int(rng.integers(1, 700)),
+             comp_rows=int(rng.integers(1, 3000)))
+    K = K1 + K2
+    S = int(rng.choice([0, 1, int(rng.integers(1, -(-K // 64) + 1))]))
+    plan = L.plan_splits(T, H, K, L.dtype_code(c["q"]), L.dtype_code(c["swa"]), num_splits=S)
+    check(c, f"random seed={seed} K1={K1} K2={K2} H={H} q={q} kv={kv} S={plan.num_splits}",
+          plan=plan)
