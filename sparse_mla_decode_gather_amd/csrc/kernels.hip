@@ -707,39 +707,37 @@ void decode_kernel(DecodeParams p) {
       return kv_lds + (tile % NSTAGE) * kTileBytes;
     };
 
+    // The wave's RPW row addresses of a tile in one VALU pass (LDS-DMA
+    // path): lane j (j < RPW) converts the slot code of row j, and each
+    // row's address is then read out of its lane into SGPRs (two
+    // v_readlane per row instead of a scalar chain of selects and a 64-bit
+    // multiply per row).  Slots past n_act read the last active row
+    // (slots[n_act - 1]).
+    auto lane_row_addr = [&](int tile) -> uint64_t {
+      const int sl = min(tile * kTile + wave_u * RPW + (lane & (RPW - 1)), n_act - 1);
+      const int code = slots[sl];
+      const uint8_t* base = code < 0 ? p.comp : p.swa;
+      return (uint64_t)(uintptr_t)(base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
+    };
+    auto row_of_lane = [&](uint64_t a, int jj) -> const uint8_t* {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, jj);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), jj);
+      return (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+    };
+
     if constexpr (USE_DMA) {
       // LDS-DMA gather: one instruction moves one 1 KB row, lane i's 16 B
       // landing at row base + 16 i.  Each wave gathers RPW rows per tile.
       const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
       const uint32_t lane_off = (uint32_t)lane * 16u;
-      // The wave's RPW slot codes of a tile are consecutive in slots[]:
-      // fetch them with wide LDS reads (one wait), then issue the rows.
-      // Reads past n_act stay inside slots[] (kSeg is a multiple of 32)
-      // and are replaced by the last active row.
-      const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
-      auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
-        const int s0 = tile * kTile + wave_u * RPW;
-#pragma unroll
-        for (int q = 0; q < RPW / 4; ++q) {
-          const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
-        }
-      };
-      auto issue_row = [&](int tile, int jj, const int (&codes)[RPW]) {
+      auto issue_row = [&](int tile, int jj, uint64_t addr) {
         const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
-        const int s0 = tile * kTile + wave_u * RPW;
-        int code = __builtin_amdgcn_readfirstlane(codes[jj]);
-        code = (s0 + jj < n_act) ? code : last_code;
-        const uint8_t* base = code < 0 ? p.comp : p.swa;
-        const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
-        lds_dma_row16(row, lane_off, dst + (wave_u * RPW + jj) * kRowPitch);
+        lds_dma_row16(row_of_lane(addr, jj), lane_off, dst + (wave_u * RPW + jj) * kRowPitch);
       };
       auto issue = [&](int tile) {
-        int codes[RPW];
-        fetch_codes(tile, codes);
+        const uint64_t addr = lane_row_addr(tile);
 #pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) issue_row(tile, jj, codes);
+        for (int jj = 0; jj < RPW; ++jj) issue_row(tile, jj, addr);
       };
       // wait until this wave's rows of `tile` landed, given the last tile
       // issued so far
@@ -762,13 +760,12 @@ void decode_kernel(DecodeParams p) {
         // it run (RPW rows, spread over the 32 MFMAs).
         const int nxt = it + NSTAGE - 1;
         const bool do_issue = kSteady || nxt < ntiles;
-        int codes[RPW];
-        fetch_codes(do_issue ? nxt : it, codes);
+        const uint64_t addr = lane_row_addr(do_issue ? nxt : it);
         const f32x16 sv = qk(stage(it), [&](int q) {
           static_assert(RPW == 8 || RPW == 16, "rows per wave");
 #pragma unroll
           for (int r = 0; r < RPW / 8; ++r)
-            if (do_issue) issue_row(nxt, q * (RPW / 8) + r, codes);
+            if (do_issue) issue_row(nxt, q * (RPW / 8) + r, addr);
         });
         serial_point(true);
         bf16x8 pf[2];
@@ -787,6 +784,10 @@ void decode_kernel(DecodeParams p) {
       static_assert(KV_FP8, "register staging serves FP8 rows");
       constexpr int VW = 2;                       // dwords per lane per row
       typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
+      // (The rows' addresses here come from a scalar chain per row rather
+      // than lane_row_addr: with the loads' registers live, the readouts'
+      // VALU-to-SGPR waits cost more than they save; measured 7-10% slower
+      // on FP8 and packed rows.)
       const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
       const uint32_t lane_off = (uint32_t)lane * (VW * 4);
       const PackedLane pl = packed_lane(lane);   // packed rows only
