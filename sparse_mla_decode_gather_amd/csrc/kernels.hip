@@ -761,12 +761,35 @@ void decode_kernel(DecodeParams p) {
         const int nxt = it + NSTAGE - 1;
         const bool do_issue = kSteady || nxt < ntiles;
         const uint64_t addr = lane_row_addr(do_issue ? nxt : it);
-        const f32x16 sv = qk(stage(it), [&](int q) {
-          static_assert(RPW == 8 || RPW == 16, "rows per wave");
+        static_assert(RPW == 8 || RPW == 16, "rows per wave");
+        constexpr int PER = RPW / 8;               // rows issued per hook
+        f32x16 sv;
+        if constexpr (kSteady) {
+          // Each hook issues rows read out at the hook before (at least four
+          // MFMAs earlier), so the loads need no wait states for their
+          // freshly written address registers.
+          const uint32_t tbase = lds_base + (uint32_t)((nxt % NSTAGE) * kTileBytes) +
+                                 (uint32_t)(wave_u * RPW * kRowPitch);
+          const uint8_t* rr[PER];
 #pragma unroll
-          for (int r = 0; r < RPW / 8; ++r)
-            if (do_issue) issue_row(nxt, q * (RPW / 8) + r, addr);
-        });
+          for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(addr, r);
+          sv = qk(stage(it), [&](int q) {
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+              lds_dma_row16<false, true>(rr[r], lane_off,
+                                         tbase + (uint32_t)((q * PER + r) * kRowPitch));
+            if (q + 1 < 8) {
+#pragma unroll
+              for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(addr, (q + 1) * PER + r);
+            }
+          });
+        } else {
+          sv = qk(stage(it), [&](int q) {
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+              if (do_issue) issue_row(nxt, q * PER + r, addr);
+          });
+        }
         serial_point(true);
         bf16x8 pf[2];
         softmax(sv, n_in(it), pf, steady);
