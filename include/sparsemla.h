@@ -187,9 +187,10 @@ typedef struct smla_decode_args {
  *   forces S = clamp(override, 1, min(num_chunks, SMLA_MAX_SPLITS));
  *   num_cus <= 0 queries the current device's compute-unit count once and
  *   caches it per device.
- *   The dtypes are checked but do not change the plan: every row format is
- *   widened and multiplied on the BF16 MFMA, so a split's time follows its
- *   row count.
+ *   Every row format is widened and multiplied on the BF16 MFMA, so a
+ *   split's time follows its row count, not its bytes.  The dtypes change
+ *   the plan only at H=64: BF16 q with BF16 rows runs one four-wave
+ *   workgroup per compute unit, the other pairs two two-wave workgroups.
  * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1, K > SMLA_MAX_PLAN_COLUMNS
  * or a NULL out_plan,
  * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128},

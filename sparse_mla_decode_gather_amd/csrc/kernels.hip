@@ -12,12 +12,13 @@
 //
 // Kernel design (ours, for CDNA4; the pages' TRTLLM-gen / CuTe kernels are
 // prior art only):
-//  * One workgroup of 4 wave64s (2 at H=64) per (token, split), one wave per
-//    SIMD.  All H heads of the token live in the workgroup, so each gathered
+//  * One workgroup of 4 wave64s (2 at H=64 with FP8 or packed rows) per
+//    (token, split), one wave per SIMD.  All H heads of the token live in the workgroup, so each gathered
 //    row is read from HBM once per (token, split) and reused by every head.
 //  * The split's table columns are compacted first (masked, -1, truncated
 //    and out-of-range slots are dropped), so tiles are dense.
-//  * Rows are gathered 32 at a time into row-major LDS tiles with a padded
+//  * Rows are gathered 32 at a time (64 in decode_h64_kernel) into
+//    row-major LDS tiles with a padded
 //    pitch (conflict-free row and transposed reads), by LDS-DMA for BF16
 //    rows and through registers for FP8 rows and packed block-scaled rows
 //    (widened to BF16 on the way; every E4M3FN value, and every E4M3FN value
@@ -31,10 +32,12 @@
 //    first tile and left alone; a tile exceeding it by more than 2^64 makes
 //    the split start over with the higher reference, so O is never rescaled
 //    and the result is exact up to rounding.
-//  * decode_kernel (H=64): wave w computes S and O for its own 32 heads.
-//    decode_hd_kernel (H=128): wave w computes S for 32 heads but O for a
-//    quarter of the output dims of all heads, with P exchanged through LDS
-//    (see there).  FP8 q and FP8 rows are widened exactly to BF16 and
+//  * decode_kernel (H=64, FP8 or packed rows): wave w computes S and O for
+//    its own 32 heads.  decode_hd_kernel (H=128): wave w computes S for 32
+//    heads but O for a quarter of the output dims of all heads, with P
+//    exchanged through LDS (see there).  decode_h64_kernel (H=64, BF16 q
+//    and rows): the same split of O over four waves, with S of a 64-row
+//    tile split over the waves by head block and row block.  FP8 q and FP8 rows are widened exactly to BF16 and
 //    multiplied on the BF16 MFMA.
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
@@ -1682,6 +1685,449 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// split kernel, H = 64 with BF16 rows: four waves, 64-row tiles
+// ---------------------------------------------------------------------------
+//
+// decode_kernel gives each of its two waves 32 heads for both products, so
+// two workgroups share a CU and every wave reads the whole V tile.  Here one
+// workgroup of four waves fills the CU: wave w computes S^T and the softmax
+// of heads [32(w&1), +32) over rows [32(w>>1), +32) of a 64-row tile, and
+// O^T for the output dims [128w, +128) of all 64 heads over all 64 rows, with
+// P^T exchanged through LDS in the O^T MFMAs' B-operand layout (as in
+// decode_hd_kernel).  Two LDS stages of 64 rows: the rows of tile i+1 go out
+// by LDS-DMA during the S^T MFMAs of tile i.  The two waves that share a
+// head block share its reference max: the first tile's is the max over both
+// row blocks (exchanged through LDS), and a restart takes the larger of the
+// two waves' raised maxima.  The normaliser adds the two waves' sums.
+template <bool SPLIT, bool GEN, bool SERIAL = false>
+__global__ __launch_bounds__(256, 1)
+void decode_h64_kernel(DecodeParams p) {
+  constexpr int NW = 4, H = 64, NT = 256;
+  constexpr int TR = 64;                  // tile rows
+  constexpr int RPW = TR / NW;            // rows each wave gathers per tile
+  constexpr int NSTAGE = 2;
+  constexpr int kSegHd = 2048;            // table columns per pass
+  constexpr int CPT = kSegHd / NT;        // columns per thread in compaction
+  constexpr int NDB = kD / NW / 32;       // 32-dim blocks of O per wave
+  constexpr int NHB = H / 32;             // head blocks
+  constexpr int NKS = TR / 16;            // 16-row steps of O^T
+  constexpr int kStageBytes = TR * kRowPitch;
+  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kStageBytes];
+  __shared__ __attribute__((aligned(16))) u32x4 p_lds[NHB * NKS * 64];
+  __shared__ __attribute__((aligned(16))) int32_t slots[kSegHd + TR];
+  __shared__ float inv_lds[H];
+  __shared__ float pair_lds[2][H];        // per row block: a head's max, then its sum
+  __shared__ int32_t wave_cnt[NW];
+  __shared__ int32_t restart_flag;
+  auto serial_point = [](bool wait_loads) {
+    if constexpr (SERIAL) {
+      if (wait_loads) wait_vmcnt<0>();
+      __syncthreads();
+    }
+  };
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int l32 = lane & 31;
+  const int kg = lane >> 5;
+  const int hbs = wave & 1, rbs = wave >> 1;   // this wave's S^T block
+  const int head = hbs * 32 + l32;             // head of this lane's S^T column
+
+  // XCD-aware work mapping, longest item first when a CU gets more than
+  // one (see decode_hd_kernel)
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int q8 = nblk >> 3, r8 = nblk & 7;
+  const int lo = xcd * q8 + min(xcd, r8);
+  int item = lo + (blockIdx.x >> 3);
+  {
+    const int cnt = q8 + (xcd < r8 ? 1 : 0);
+    const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
+                            : p.topk_lens != nullptr;
+    if (p.rank_items && ragged && cnt > 1 && cnt <= NT) {
+      const int tid = threadIdx.x;
+      int my_len = -1;
+      if (tid < cnt) {
+        const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
+        int a, b;
+        token_length_loads<GEN>(p, ti, a, b);
+        TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
+        token_lengths<GEN>(p, a, b, ti_tab);
+        const int c0 = si * p.split_cols, c1 = c0 + p.split_cols;
+        my_len = max(0, min(ti_tab.L1, c1) - c0);
+        if constexpr (GEN)
+          my_len += max(0, min(ti_tab.P + ti_tab.L2, c1) - max(ti_tab.P, c0));
+        slots[tid] = my_len;
+      }
+      __syncthreads();
+      if (tid < cnt) {
+        int rank = 0;
+        for (int k = 0; k < cnt; ++k) {
+          const int lk = slots[k];
+          rank += (lk > my_len || (lk == my_len && k < tid)) ? 1 : 0;
+        }
+        if (rank == (int)(blockIdx.x >> 3)) slots[kSegHd] = lo + tid;
+      }
+      __syncthreads();
+      item = slots[kSegHd];
+      __syncthreads();   // slots[] is rewritten by the compaction
+    }
+  }
+  const int t = item / p.S;
+  const int s = item - t * p.S;
+
+  // table entries, then Q (see decode_hd_kernel)
+  const int c_begin = s * p.split_cols;
+  const int c_cap = min(p.K, c_begin + p.split_cols);
+  TokenTable<GEN, false> tt = token_table<GEN, false>(p, t);
+  int len_a, len_b;
+  token_length_loads<GEN>(p, t, len_a, len_b);
+  int rv[CPT];
+  auto load_idx = [&](int seg0, int seg_hi) {
+    const int cb = seg0 + threadIdx.x * CPT;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) rv[k] = (cb + k < seg_hi) ? tt.raw(p, cb + k) : -1;
+  };
+  load_idx(c_begin, min(c_cap, c_begin + kSegHd));
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 qf[32];
+  {
+    const size_t qrow = ((size_t)t * H + head) * kD;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      const int d0 = kk * 16 + kg * 8;
+      qf[kk] = __builtin_bit_cast(
+          bf16x8, *(const global_u32x4*)((const uint16_t*)p.q + qrow + d0));
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const bool lens_ok = token_lengths<GEN>(p, len_a, len_b, tt);
+  if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
+  const int c_end = min(tt.end(), c_cap);
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  bool ref_set = false;
+  // O^T: o[db][hb] holds dims 128w + 32db + 8(i/4) + 4kg + i%4 of head
+  // 32hb + l32.
+  f32x16 o[NDB][NHB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+
+  const int qk_off = (rbs * 32 + l32) * kRowPitch + kg * 16;
+  const int i16 = lane & 15, grp = lane >> 4;
+  const int tr_off = (4 * (grp >> 1) + (i16 >> 2)) * kRowPitch +
+                     (16 * (grp & 1) + 4 * (i16 & 3)) * 2 + wave * (NDB * 64);
+  const uint32_t lane_off = (uint32_t)lane * 16u;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
+  if (threadIdx.x == 0) restart_flag = 0;
+  bool need_sticky = false;
+
+  // S^T of this wave's 32 rows of the tile at tb; every4(q) after MFMA 4q+3
+  constexpr int kLead = 4;
+  auto qk = [&](const uint8_t* tb, auto&& every4) -> f32x16 {
+    bf16x8 a[kLead];
+#pragma unroll
+    for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
+    f32x16 acc;
+#pragma unroll
+    for (int kk = 0; kk < 32; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
+      else mfma_qk(acc, a[kk % kLead], qf[kk]);
+      if (kk + kLead < 32)
+        a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
+      if ((kk & 3) == 3) {
+        __builtin_amdgcn_sched_barrier(0);
+        every4(kk >> 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return acc;
+  };
+  auto vfrag = [&](const uint8_t* vt, int f) -> bf16x8 {
+    const uint8_t* vb = vt + tr_off + (16 * (f >> 2)) * kRowPitch + (f & 3) * 64;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(vb));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
+    return __builtin_bit_cast(bf16x8,
+                              __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pfrag = [&](int h, int hb) -> bf16x8 {
+    return __builtin_bit_cast(bf16x8, p_lds[(hb * NKS + h) * 64 + lane]);
+  };
+  // O^T += V^T P^T over the tile's 64 rows.  MFMA k: 16-row step h = k/8,
+  // dim block db = (k/2) % 4, head block hb = k % 2; V^T fragment f = 4h + db
+  // is read two fragments ahead, P^T of step h+1 during step h.
+  auto ot = [&](const uint8_t* vt) {
+    bf16x8 v[3], pf[2][NHB];
+    pf[0][0] = pfrag(0, 0);
+    pf[0][1] = pfrag(0, 1);
+    v[0] = vfrag(vt, 0);
+    v[1] = vfrag(vt, 1);
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int h = k >> 3, db = (k >> 1) & 3, hb = k & 1, f = 4 * h + db;
+      o[db][hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[f % 3], pf[h & 1][hb],
+                                                         o[db][hb], 0, 0, 0);
+      if (hb == 1 && f + 2 < 4 * NKS) v[(f + 2) % 3] = vfrag(vt, f + 2);
+      if ((k & 7) == 3 && h + 1 < NKS) {
+        pf[(h + 1) & 1][0] = pfrag(h + 1, 0);
+        pf[(h + 1) & 1][1] = pfrag(h + 1, 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bool again;
+  bool first_seg = true;
+  do {
+  again = false;
+  for (int seg0 = c_begin; seg0 < c_end && !again; seg0 += kSegHd) {
+    const int seg1 = min(c_end, seg0 + kSegHd);
+
+    // ---- compact the active slots of this segment (see decode_hd_kernel) --
+    __syncthreads();
+    if (!first_seg) {
+      load_idx(seg0, seg1);
+      wait_vmcnt<0>();
+    }
+    first_seg = false;
+    const int cb = seg0 + threadIdx.x * CPT;
+    uint32_t actm = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = cb + k;
+      const int r = rv[k];
+      if (r != -1 && c < seg1 && tt.live(c)) {
+        const int64_t rows = tt.swa(c) ? p.swa_rows : p.comp_rows;
+        if (r >= 0 && (int64_t)r < rows) actm |= 1u << k;
+        else if (p.validate) record_error(p.err, 1, t, c);
+      }
+    }
+    const int cnt = __popc(actm);
+    static_assert(CPT < 16, "four ballots cover cnt");
+    int incl = cnt;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint64_t m = __ballot((cnt >> b) & 1);
+      incl += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    }
+    if (lane == 63) wave_cnt[wave] = incl;
+    __syncthreads();
+    int pos = incl - cnt, n_act = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int cw = wave_cnt[w2];
+      pos += (w2 < wave) ? cw : 0;
+      n_act += cw;
+    }
+    int last = 0;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      if ((actm >> k) & 1u) {
+        last = tt.swa(cb + k) ? rv[k] : (int)((uint32_t)rv[k] | 0x80000000u);
+        slots[pos++] = last;
+      }
+    }
+    const int ntiles = (n_act + TR - 1) / TR;
+    if (cnt > 0 && pos == n_act) {
+      for (int i = n_act; i < ntiles * TR; ++i) slots[i] = last;
+    }
+    __syncthreads();
+    if (ntiles > 0) {
+      auto stage = [&](int tile) -> const uint8_t* {
+        return kv_lds + (tile % NSTAGE) * kStageBytes;
+      };
+      // lane j < RPW: the address of this wave's row j of `tile`
+      auto lane_row_addr = [&](int tile) -> uint64_t {
+        const int code = slots[tile * TR + wave_u * RPW + (lane & (RPW - 1))];
+        const uint8_t* base = code < 0 ? p.comp : p.swa;
+        return (uint64_t)(uintptr_t)(base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
+      };
+      auto row_of_lane = [&](uint64_t a, int jj) -> const uint8_t* {
+        const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, jj);
+        const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), jj);
+        return (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
+      };
+      auto tile_lds = [&](int tile) -> uint32_t {
+        return lds_base + (uint32_t)((tile % NSTAGE) * kStageBytes) +
+               (uint32_t)(wave_u * RPW * kRowPitch);
+      };
+      {
+        const uint64_t a0 = lane_row_addr(0);
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj)
+          lds_dma_row16(row_of_lane(a0, jj), lane_off, tile_lds(0) + (uint32_t)(jj * kRowPitch));
+      }
+      for (int it = 0; it < ntiles; ++it) {
+        wait_vmcnt<0>();                // this wave's rows of tile it landed
+        __syncthreads();                // every wave's; O^T of tile it-1 done
+        const bool more = it + 1 < ntiles;
+        // the rows of tile it+1 go out during the S^T MFMAs, two per four
+        // MFMAs, each read out at the hook before
+        const uint64_t an = lane_row_addr(more ? it + 1 : it);
+        const uint32_t dn = tile_lds(it + 1);
+        constexpr int PER = RPW / 8;
+        const uint8_t* rr[PER];
+#pragma unroll
+        for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(an, r);
+        f32x16 sv = qk(stage(it), [&](int q) {
+          if (more) {
+#pragma unroll
+            for (int r = 0; r < PER; ++r)
+              lds_dma_row16<false, true>(rr[r], lane_off, dn + (uint32_t)((q * PER + r) * kRowPitch));
+          }
+          if (q + 1 < 8) {
+#pragma unroll
+            for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(an, (q + 1) * PER + r);
+          }
+        });
+        mfma_qk_drain(sv);
+        const int nt = min(TR, n_act - it * TR);
+        if (nt < TR) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            sv[i] = (rbs * 32 + tile_row_of_reg(i, kg) < nt) ? sv[i] : -INFINITY;
+        }
+        serial_point(true);
+        // ---- softmax of this wave's 32 rows ---------------------------------
+        float smax = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+        for (int i = 3; i < 15; i += 2) smax = fmaxf(fmaxf(smax, sv[i]), sv[i + 1]);
+        smax = max_with_other_half(fmaxf(smax, sv[15]));
+        float tmax = smax * p.scale_log2;          // scale_log2 > 0
+        if (!ref_set) {
+          // the first tile: the reference is the max over both row blocks
+          if (kg == 0) pair_lds[rbs][head] = tmax;
+          __syncthreads();
+          m_run = fmaxf(pair_lds[0][head], pair_lds[1][head]);
+          ref_set = true;
+        }
+        const bool need = tmax > m_run + kRefSlack;
+        m_run = need ? tmax : m_run;
+        need_sticky |= need;
+        float lsum = 0.f;
+        u32x4 pk[2];
+#pragma unroll
+        for (int j = 0; j < 16; j += 2) {
+          const float p0 = fast_exp2(__builtin_fmaf(sv[j], p.scale_log2, -m_run));
+          const float p1 = fast_exp2(__builtin_fmaf(sv[j + 1], p.scale_log2, -m_run));
+          lsum += p0 + p1;
+          pk[j >> 3][(j & 7) >> 1] = pack_bf16x2(p0, p1);
+        }
+        l_run += lsum;
+        p_lds[(hbs * NKS + 2 * rbs + 0) * 64 + lane] = pk[0];
+        p_lds[(hbs * NKS + 2 * rbs + 1) * 64 + lane] = pk[1];
+        __syncthreads();                // P^T of tile it published
+        ot(stage(it));
+        serial_point(false);
+      }
+    }
+    if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
+    __syncthreads();
+    again = restart_flag != 0;
+  }
+  if (again) {
+    // Rare: start the split over with the raised reference maxima, the same
+    // for the two waves of a head block.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) restart_flag = 0;
+    if (kg == 0) pair_lds[rbs][head] = m_run;
+    __syncthreads();
+    m_run = fmaxf(pair_lds[0][head], pair_lds[1][head]);
+    need_sticky = false;
+    l_run = 0.f;
+    float zero;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][hb][i] = zero;
+  }
+  } while (again);
+
+  // ---- epilogue -------------------------------------------------------------
+  // A head's sum: this wave's 32 rows (both halves of the wave), plus the
+  // other row block's.
+  __syncthreads();                      // pair_lds is free
+  {
+    const float lb = l_run + __shfl_xor(l_run, 32);
+    if (kg == 0) pair_lds[rbs][head] = lb;
+  }
+  __syncthreads();
+  if (rbs == 0) {
+    float l = pair_lds[0][head] + pair_lds[1][head];
+    float m = m_run;
+    float inv, lse;
+    if constexpr (SPLIT) {
+      inv = (l > 0.f) ? p.bmm2 / l : 0.f;
+      lse = (l > 0.f) ? m + fast_log2(l) : -INFINITY;
+    } else {
+      float fac = 1.f;
+      if (p.sinks) {
+        const float sl = p.sinks[head] * kLog2e;
+        const float mm = fmaxf(m, sl);
+        fac = fast_exp2(m - mm);        // 0 when nothing was active (m = -inf)
+        l = l * fac + fast_exp2(sl - mm);
+        m = mm;
+      }
+      inv = (l > 0.f) ? fac * p.bmm2 / l : 0.f;
+      lse = (l > 0.f) ? p.lse_scale * (m + fast_log2(l)) : -INFINITY;
+    }
+    if (kg == 0) {
+      inv_lds[head] = inv;
+      if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
+      else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
+    }
+  }
+  __syncthreads();
+  // O goes out through LDS as whole 1 KB head rows (the tiles are no longer
+  // in use): every wave writes its 128 dims of each head, then each wave
+  // stores whole rows.
+  constexpr int kOutPitch = kD * 2 + 16;
+  static_assert(H * kOutPitch <= NSTAGE * kStageBytes, "epilogue staging");
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb) {
+    const float inv = inv_lds[hb * 32 + l32];
+    uint8_t* rowp = kv_lds + (hb * 32 + l32) * kOutPitch + wave * (NDB * 64) + kg * 8;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        u32x2 w;
+        w[0] = pack_bf16x2(o[db][hb][4 * a] * inv, o[db][hb][4 * a + 1] * inv);
+        w[1] = pack_bf16x2(o[db][hb][4 * a + 2] * inv, o[db][hb][4 * a + 3] * inv);
+        *(u32x2*)(rowp + db * 64 + a * 16) = w;
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < H / NW; ++r) {
+    const int hh = r * NW + wave;
+    const u32x4 v = *(const u32x4*)(kv_lds + hh * kOutPitch + lane * 16);
+    uint16_t* dst;
+    if constexpr (SPLIT)
+      dst = p.mid_out + (((size_t)t * H + hh) * p.S + s) * kD;
+    else
+      dst = (uint16_t*)p.out + ((size_t)t * H + hh) * kD;
+    *(u32x4*)(dst + lane * 8) = v;
+  }
+}
+
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool STREAM, bool PACKED = false,
           bool SERIAL = false>
 __global__ __launch_bounds__(256, 1)
@@ -1915,6 +2361,29 @@ hipError_t launch_decode_hd_packed(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// BF16 q and rows at H = 64: the four-wave kernel.
+hipError_t launch_decode_h64(const DecodeParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)(p.T * p.S));
+  const bool gen = p.segmented != 0;
+  if (p.serial) {            // combined table only (checked on the host)
+    if (gen) return hipErrorInvalidValue;
+    if (p.S > 1)
+      hipLaunchKernelGGL((decode_h64_kernel<true, false, true>), grid, dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode_h64_kernel<false, false, true>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.S > 1 && gen)
+    hipLaunchKernelGGL((decode_h64_kernel<true, true>), grid, dim3(256), 0, stream, p);
+  else if (p.S > 1)
+    hipLaunchKernelGGL((decode_h64_kernel<true, false>), grid, dim3(256), 0, stream, p);
+  else if (gen)
+    hipLaunchKernelGGL((decode_h64_kernel<false, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_h64_kernel<false, false>), grid, dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <int NW, bool QF, bool KF, bool PK = false>
 hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
@@ -1988,7 +2457,7 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
   }
   const bool qf = q_dtype != 0, kf = kv_dtype != 0;
   if (p.H == 64) {
-    if (!qf && !kf) return launch_decode_t<2, false, false>(p, stream);
+    if (!qf && !kf) return launch_decode_h64(p, stream);
     if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
     return launch_decode_t<2, false, true>(p, stream);
   }

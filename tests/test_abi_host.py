@@ -641,6 +641,9 @@ def test_flags_unknown_bits_and_serial_pipeline_forms(so):
     (128, 128, 2048, 0, 2), (512, 128, 2048, 0, 1),
     (512, 128, 2048, 1, 1),    # speculative decode (FP8 rows, BF16 q)
     (16, 128, 512, 1, 4),      # FP8 rows plan by row count, not bytes (was 1)
+    # H=64, BF16 q and rows: one four-wave workgroup per CU
+    (16, 64, 2048, 0, 11), (64, 64, 512, 0, 2), (128, 64, 1024, 0, 2),
+    (512, 64, 2048, 0, 1),
 ])
 def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S):
     """The planner's picks for the benchmarked shapes on a 256-CU device
@@ -648,3 +651,16 @@ def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S):
     MI355X; the cost model is deterministic, so these are exact)."""
     q = 1 if (kv == 1 and H == 64) else 0
     assert plan(T, H, K, q=q, kv=kv, cus=256).num_splits == S
+
+
+def test_plan_h64_depends_on_the_row_format():
+    """At H=64 BF16 q with BF16 rows runs one workgroup per CU and gathers a
+    row in half the time of the two-wave kernel the other formats run (two
+    per CU), so the same shape can get fewer splits."""
+    assert plan(128, 64, 1024, q=0, kv=0, cus=256).num_splits == 2
+    assert plan(128, 64, 1024, q=0, kv=1, cus=256).num_splits == 4
+    assert plan(128, 64, 1024, q=1, kv=1, cus=256).num_splits == 4
+    assert plan(128, 64, 1024, q=0, kv=2, cus=256).num_splits == 4
+    for kv in (0, 1, 2):       # H=128: the format never changes the plan
+        assert plan(128, 128, 1024, q=0, kv=kv, cus=256).num_splits == \
+            plan(128, 128, 1024, q=0, kv=0, cus=256).num_splits

@@ -428,8 +428,9 @@ def test_streaming_row_loads_match_plain_loads():
           what="streaming loads vs oracle")
 
 
+@pytest.mark.parametrize("H", [64, 128])
 @pytest.mark.parametrize("T", [256, 250])     # 250: XCD ranges of unequal size
-def test_ragged_batch_order_does_not_change_any_token(T):
+def test_ragged_batch_order_does_not_change_any_token(T, H):
     """Workgroups start the items of their XCD longest first, so permuting
     the tokens of a ragged batch reassigns every item to another workgroup;
     each token's output and LSE must stay bit-identical (unsplit and split),
@@ -441,7 +442,7 @@ def test_ragged_batch_order_does_not_change_any_token(T):
         np.stack([g.choice(600, 128, replace=False) for _ in range(T)]),
         np.stack([g.choice(4000, K - 128, replace=False) for _ in range(T)])], axis=1)
     lens = g.integers(1, K + 1, size=T)
-    w = custom(idx, lens, swa_rows=600, comp_rows=4000, seed=23)
+    w = custom(idx, lens, H=H, swa_rows=600, comp_rows=4000, seed=23)
     perm = torch.as_tensor(g.permutation(T)).cuda()
     wp = W.Workload(
         name="permuted", T=T, H=w.H, K=K, q=w.q[perm].contiguous(), q_dtype=w.q_dtype,
@@ -450,8 +451,8 @@ def test_ragged_batch_order_does_not_change_any_token(T):
         seq_lens=w.seq_lens[perm].contiguous(), cum_seq_lens_q=None, sinks=w.sinks,
         bmm1_scale=w.bmm1_scale, bmm2_scale=w.bmm2_scale, lse_scale=w.lse_scale)
     for S in (1, 3):
-        log(f"[parity] ragged batch T={T} permuted, {S} split(s)")
-        plan = L.plan_splits(T, 128, K, num_splits=S)
+        log(f"[parity] ragged batch T={T} H={H} permuted, {S} split(s)")
+        plan = L.plan_splits(T, H, K, num_splits=S)
         a, la = run_decode(w, plan=plan)
         b, lb = run_decode(wp, plan=plan)
         same_bits(a[perm], b, str(S))

@@ -169,21 +169,22 @@ def test_segments_validate_reports_virtual_columns_and_lengths():
     assert L.get_device_error(ws)[:2] == (2, 1)
 
 
-def test_ragged_segments_batch_order_does_not_change_any_token():
+@pytest.mark.parametrize("H", [64, 128])
+def test_ragged_segments_batch_order_does_not_change_any_token(H):
     """Items start longest first within each XCD (ranked by the active
     columns of both tables); permuting the tokens of a ragged batch moves
     every item to another workgroup and must leave each token's bits
     unchanged, unsplit and split."""
     need_gpu()
     T, K1, K2 = 256, 128, 1920
-    c = make(T, K1, K2, swa_rows=600, comp_rows=4000, seed=41)
+    c = make(T, K1, K2, H=H, swa_rows=600, comp_rows=4000, seed=41)
     perm = torch.as_tensor(np.random.default_rng(5).permutation(T)).cuda()
     cp = dict(c)
     for k in ("q", "si", "ei", "sl", "el"):
         cp[k] = c[k][perm].contiguous()
     for S in (1, 2):
-        log(f"[segments] ragged batch T={T} permuted, {S} split(s)")
-        plan = L.plan_splits(T, 128, K1 + K2, num_splits=S)
+        log(f"[segments] ragged batch T={T} H={H} permuted, {S} split(s)")
+        plan = L.plan_splits(T, H, K1 + K2, num_splits=S)
         a, la = run(c, plan=plan)
         b, lb = run(cp, plan=plan)
         same_bits(a[perm], b, str(S))
