@@ -470,7 +470,8 @@ template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = f
           bool SERIAL = false>
 __global__ __launch_bounds__(NW * 64, 1)
 void decode_kernel(DecodeParams p) {
-  static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
+  static_assert(KV_FP8, "FP8 or packed rows (BF16 rows: decode_h64_kernel)");
+  static_assert(!PACKED || !Q_FP8, "packed rows: BF16 q");
   // all loads of the wave landed and every wave arrived (SERIAL only)
   auto serial_point = [](bool wait_loads) {
     if constexpr (SERIAL) {
@@ -481,12 +482,10 @@ void decode_kernel(DecodeParams p) {
   constexpr int H = NW * 32;              // one wave per 32 heads
   constexpr int NT = NW * 64;
   constexpr int RPW = kTile / NW;         // tile rows each wave gathers
-  // Row gather into NSTAGE LDS tiles.  BF16 rows use LDS-DMA loads, which
-  // need no registers (this kernel has none to spare); FP8 rows go through
-  // registers (8 bytes per lane) and are widened to BF16 on the way.  The
+  // Row gather into NSTAGE LDS tiles through registers (8 bytes of an FP8
+  // row per lane, 16 of a packed row), widened to BF16 on the way.  The
   // loads for tile it+NSTAGE-1 are in flight while tile it is computed.
-  constexpr bool USE_DMA = !KV_FP8;
-  constexpr int NSTAGE = KV_FP8 ? 2 : (NW == 4 ? 4 : 2);
+  constexpr int NSTAGE = 2;
   __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
   __shared__ __attribute__((aligned(16))) int32_t slots[kSeg];
   __shared__ int32_t wave_cnt[NW];
@@ -710,191 +709,95 @@ void decode_kernel(DecodeParams p) {
       return kv_lds + (tile % NSTAGE) * kTileBytes;
     };
 
-    // The wave's RPW row addresses of a tile in one VALU pass (LDS-DMA
-    // path): lane j (j < RPW) converts the slot code of row j, and each
-    // row's address is then read out of its lane into SGPRs (two
-    // v_readlane per row instead of a scalar chain of selects and a 64-bit
-    // multiply per row).  Slots past n_act read the last active row
-    // (slots[n_act - 1]).
-    auto lane_row_addr = [&](int tile) -> uint64_t {
-      const int sl = min(tile * kTile + wave_u * RPW + (lane & (RPW - 1)), n_act - 1);
-      const int code = slots[sl];
-      const uint8_t* base = code < 0 ? p.comp : p.swa;
-      return (uint64_t)(uintptr_t)(base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes);
-    };
-    auto row_of_lane = [&](uint64_t a, int jj) -> const uint8_t* {
-      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)a, jj);
-      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(a >> 32), jj);
-      return (const uint8_t*)(uintptr_t)((uint64_t)lo | ((uint64_t)hi << 32));
-    };
-
-    if constexpr (USE_DMA) {
-      // LDS-DMA gather: one instruction moves one 1 KB row, lane i's 16 B
-      // landing at row base + 16 i.  Each wave gathers RPW rows per tile.
-      const uint32_t lds_base = (uint32_t)(uintptr_t)kv_lds;
-      const uint32_t lane_off = (uint32_t)lane * 16u;
-      auto issue_row = [&](int tile, int jj, uint64_t addr) {
-        const uint32_t dst = lds_base + (uint32_t)((tile % NSTAGE) * kTileBytes);
-        lds_dma_row16(row_of_lane(addr, jj), lane_off, dst + (wave_u * RPW + jj) * kRowPitch);
-      };
-      auto issue = [&](int tile) {
-        const uint64_t addr = lane_row_addr(tile);
+    // Register-staged gather of FP8 rows: lane `lane` carries 8 B of a row,
+    // widened to BF16 when written to LDS.  The loads of tile it+NSTAGE-1
+    // are issued while the S^T MFMAs of tile it run and written to LDS
+    // after its O^T MFMAs, into the stage tile it-1 used.
+    constexpr int VW = 2;                       // dwords per lane per row
+    typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
+    // (The rows' addresses here come from a scalar chain per row rather
+    // than from one VALU pass read out per row, as in the LDS-DMA kernels:
+    // with the loads' registers live, the readouts' VALU-to-SGPR waits
+    // cost more than they save; measured 7-10% slower on FP8 and packed
+    // rows.)
+    const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
+    const uint32_t lane_off = (uint32_t)lane * (VW * 4);
+    const PackedLane pl = packed_lane(lane);   // packed rows only
+    stage_t st[RPW];
+    auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
+      const int s0 = tile * kTile + wave_u * RPW;
 #pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) issue_row(tile, jj, addr);
-      };
-      // wait until this wave's rows of `tile` landed, given the last tile
-      // issued so far
-      auto wait_tile = [&](int tile, int last_issued) {
-        const int after = last_issued - tile;
-        if (after >= 2) wait_vmcnt<2 * RPW>();
-        else if (after == 1) wait_vmcnt<RPW>();
-        else wait_vmcnt<0>();
-      };
-      const int pro = min(NSTAGE - 1, ntiles);
-      for (int tl = 0; tl < pro; ++tl) issue(tl);
-      // STEADY iterations (the rows of a later tile go out, tile it is
-      // whole) are a compile-time variant with no branches in their body.
-      auto iteration = [&](auto steady, int it) {
-        constexpr bool kSteady = decltype(steady)::value;
-        if constexpr (SERIAL) wait_vmcnt<0>();
-        else wait_tile(it, min(it + NSTAGE - 2, ntiles - 1));
-        __syncthreads();            // every wave's rows landed; tile it-1 done
-        // The rows of tile it+NSTAGE-1 go out while the S^T MFMAs of tile
-        // it run (RPW rows, spread over the 32 MFMAs).
-        const int nxt = it + NSTAGE - 1;
-        const bool do_issue = kSteady || nxt < ntiles;
-        const uint64_t addr = lane_row_addr(do_issue ? nxt : it);
-        static_assert(RPW == 8 || RPW == 16, "rows per wave");
-        constexpr int PER = RPW / 8;               // rows issued per hook
-        f32x16 sv;
-        if constexpr (kSteady) {
-          // Each hook issues rows read out at the hook before (at least four
-          // MFMAs earlier), so the loads need no wait states for their
-          // freshly written address registers.
-          const uint32_t tbase = lds_base + (uint32_t)((nxt % NSTAGE) * kTileBytes) +
-                                 (uint32_t)(wave_u * RPW * kRowPitch);
-          const uint8_t* rr[PER];
+      for (int q = 0; q < RPW / 4; ++q) {
+        const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
 #pragma unroll
-          for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(addr, r);
-          sv = qk(stage(it), [&](int q) {
-#pragma unroll
-            for (int r = 0; r < PER; ++r)
-              lds_dma_row16<false, true>(rr[r], lane_off,
-                                         tbase + (uint32_t)((q * PER + r) * kRowPitch));
-            if (q + 1 < 8) {
-#pragma unroll
-              for (int r = 0; r < PER; ++r) rr[r] = row_of_lane(addr, (q + 1) * PER + r);
-            }
-          });
-        } else {
-          sv = qk(stage(it), [&](int q) {
-#pragma unroll
-            for (int r = 0; r < PER; ++r)
-              if (do_issue) issue_row(nxt, q * PER + r, addr);
-          });
-        }
-        serial_point(true);
-        bf16x8 pf[2];
-        softmax(sv, n_in(it), pf, steady);
-        pv(stage(it), pf, pv_no_hook);
-        serial_point(false);
-      };
-      int it = 0;
-      for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
-      for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
-    } else {
-      // Register-staged gather of FP8 rows: lane `lane` carries 8 B of a row,
-      // widened to BF16 when written to LDS.  The loads of tile it+NSTAGE-1
-      // are issued while the S^T MFMAs of tile it run and written to LDS
-      // after its O^T MFMAs, into the stage tile it-1 used.
-      static_assert(KV_FP8, "register staging serves FP8 rows");
-      constexpr int VW = 2;                       // dwords per lane per row
-      typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
-      // (The rows' addresses here come from a scalar chain per row rather
-      // than lane_row_addr: with the loads' registers live, the readouts'
-      // VALU-to-SGPR waits cost more than they save; measured 7-10% slower
-      // on FP8 and packed rows.)
-      const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
-      const uint32_t lane_off = (uint32_t)lane * (VW * 4);
-      const PackedLane pl = packed_lane(lane);   // packed rows only
-      stage_t st[RPW];
-      auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
-        const int s0 = tile * kTile + wave_u * RPW;
-#pragma unroll
-        for (int q = 0; q < RPW / 4; ++q) {
-          const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
-        }
-      };
-      auto load_row = [&](int tile, int jj, const int (&codes)[RPW]) {
-        const int s0 = tile * kTile + wave_u * RPW;
-        int code = __builtin_amdgcn_readfirstlane(codes[jj]);
-        code = (s0 + jj < n_act) ? code : last_code;
-        const uint8_t* base = code < 0 ? p.comp : p.swa;
-        const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
-        if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
-        else st[jj] = load_row8(row, lane_off);
-      };
-      auto store_row = [&](int tile, int jj) {
-        uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
-        if constexpr (PACKED) {
-          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
-              packed_tile_bytes(st[jj], pl);
-        } else {
-          u32x4 v;
-          if constexpr (KV_FP8) v = widen_e4m3fn_x8(st[jj]);
-          else v = st[jj];
-          *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) = v;
-        }
-      };
-      auto store = [&](int tile) {
-#pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) store_row(tile, jj);
-      };
-      // prologue: tiles 0 .. NSTAGE-2 into their stages
-      for (int tl = 0; tl < min(NSTAGE - 1, ntiles); ++tl) {
-        int codes[RPW];
-        fetch_codes(tl, codes);
-#pragma unroll
-        for (int jj = 0; jj < RPW; ++jj) load_row(tl, jj, codes);
-        store(tl);
+        for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
       }
-      // STEADY iterations (the next tile is loaded, tile it is whole) are a
-      // compile-time variant with no branches in their body.
-      auto iteration = [&](auto steady, int it) {
-        constexpr bool kSteady = decltype(steady)::value;
-        __syncthreads();            // tile it stored by every wave; it-1 done
-        const int nxt = it + NSTAGE - 1;
-        const bool do_load = kSteady || nxt < ntiles;
-        int codes[RPW];
-        fetch_codes(do_load ? nxt : it, codes);
-        const f32x16 sv = qk(stage(it), [&](int q) {
+    };
+    auto load_row = [&](int tile, int jj, const int (&codes)[RPW]) {
+      const int s0 = tile * kTile + wave_u * RPW;
+      int code = __builtin_amdgcn_readfirstlane(codes[jj]);
+      code = (s0 + jj < n_act) ? code : last_code;
+      const uint8_t* base = code < 0 ? p.comp : p.swa;
+      const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+      if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
+      else st[jj] = load_row8(row, lane_off);
+    };
+    auto store_row = [&](int tile, int jj) {
+      uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
+      if constexpr (PACKED) {
+        *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
+            packed_tile_bytes(st[jj], pl);
+      } else {
+        *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
+            widen_e4m3fn_x8(st[jj]);
+      }
+    };
+    auto store = [&](int tile) {
 #pragma unroll
-          for (int r = 0; r < RPW / 8; ++r)
-            if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
-        });
-        serial_point(true);
-        bf16x8 pf[2];
-        softmax(sv, n_in(it), pf, steady);
-        if constexpr (kSteady) {
-          // The next tile's rows go to its stage (the one tile it-1 used,
-          // free since the barrier) between the O^T MFMAs, one row per two
-          // MFMAs: their loads went out during the S^T MFMAs.
-          static_assert(2 * RPW <= 32, "a row per two O^T MFMAs");
-          pv(stage(it), pf, [&](int k) {
-            if ((k & 1) == 0 && (k >> 1) < RPW) store_row(nxt, k >> 1);
-          });
-        } else {
-          pv(stage(it), pf, pv_no_hook);
-          if (do_load) store(nxt);
-        }
-        serial_point(false);
-      };
-      int it = 0;
-      for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
-      for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
+      for (int jj = 0; jj < RPW; ++jj) store_row(tile, jj);
+    };
+    // prologue: tiles 0 .. NSTAGE-2 into their stages
+    for (int tl = 0; tl < min(NSTAGE - 1, ntiles); ++tl) {
+      int codes[RPW];
+      fetch_codes(tl, codes);
+#pragma unroll
+      for (int jj = 0; jj < RPW; ++jj) load_row(tl, jj, codes);
+      store(tl);
     }
+    // STEADY iterations (the next tile is loaded, tile it is whole) are a
+    // compile-time variant with no branches in their body.
+    auto iteration = [&](auto steady, int it) {
+      constexpr bool kSteady = decltype(steady)::value;
+      __syncthreads();            // tile it stored by every wave; it-1 done
+      const int nxt = it + NSTAGE - 1;
+      const bool do_load = kSteady || nxt < ntiles;
+      int codes[RPW];
+      fetch_codes(do_load ? nxt : it, codes);
+      const f32x16 sv = qk(stage(it), [&](int q) {
+#pragma unroll
+        for (int r = 0; r < RPW / 8; ++r)
+          if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
+      });
+      serial_point(true);
+      bf16x8 pf[2];
+      softmax(sv, n_in(it), pf, steady);
+      if constexpr (kSteady) {
+        // The next tile's rows go to its stage (the one tile it-1 used,
+        // free since the barrier) between the O^T MFMAs, one row per two
+        // MFMAs: their loads went out during the S^T MFMAs.
+        static_assert(2 * RPW <= 32, "a row per two O^T MFMAs");
+        pv(stage(it), pf, [&](int k) {
+          if ((k & 1) == 0 && (k >> 1) < RPW) store_row(nxt, k >> 1);
+        });
+      } else {
+        pv(stage(it), pf, pv_no_hook);
+        if (do_load) store(nxt);
+      }
+      serial_point(false);
+    };
+    int it = 0;
+    for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
+    for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
     // did any wave's tile outgrow its reference max?
     if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
     __syncthreads();
