@@ -188,9 +188,9 @@ typedef struct smla_decode_args {
  *   num_cus <= 0 queries the current device's compute-unit count once and
  *   caches it per device.
  *   Every row format is widened and multiplied on the BF16 MFMA, so a
- *   split's time follows its row count, not its bytes.  The dtypes change
- *   the plan only at H=64: BF16 q with BF16 rows runs one four-wave
- *   workgroup per compute unit, the other pairs two two-wave workgroups.
+ *   split's time follows its row count, not its bytes.  The row format
+ *   changes the plan only at H=64, where BF16 rows (gathered straight into
+ *   LDS) cost half as much as rows staged through registers (FP8, packed).
  * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1, K > SMLA_MAX_PLAN_COLUMNS
  * or a NULL out_plan,
  * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128},

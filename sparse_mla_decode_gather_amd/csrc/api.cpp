@@ -129,21 +129,20 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     S = std::min(std::max(num_splits_override, 1),
                  std::min(num_chunks, SMLA_MAX_SPLITS));
   } else if (T > 0) {
-    // Workgroups resident per CU: one at H=128 (it holds 32 heads of O per
-    // wave in registers) and for BF16 q and rows at H=64 (the four-wave
-    // kernel, whose 64-row tiles fill the LDS), two for the other H=64
-    // forms (two waves each).
-    const bool h64_wide =
-        H == 64 && q_dtype == SMLA_DTYPE_BF16 && kv_dtype == SMLA_DTYPE_BF16;
-    const int64_t slots = (int64_t)num_cus * ((H == 64 && !h64_wide) ? 2 : 1);
+    // Workgroups resident per CU: one (at H=128 each wave holds 32 heads of
+    // O in registers; at H=64 the 64-row tiles of the four-wave kernel fill
+    // the LDS).
+    const int64_t slots = num_cus;
     // Per-row cost: the same for every row format.  Rows are widened to BF16
     // and multiplied on the BF16 MFMA, whose work per row is the same, so
     // the row count and not its bytes sets a split's time (weighting FP8
     // rows by their half-size bytes picked one split where 4-8 ran up to
-    // 1.5x faster: H=128 FP8 rows, K=512, T=16-48).  The four-wave H=64
-    // kernel gathers a row in half the time (fitted on its own sweep of
-    // forced splits, K = 512 .. 2048, T = 1 .. 512).
-    const int64_t row_w = h64_wide ? 1 : 2;
+    // 1.5x faster: H=128 FP8 rows, K=512, T=16-48).  At H=64 a BF16 row,
+    // gathered by LDS-DMA, costs half of one staged through registers (FP8
+    // and packed rows), which at H=128 the MFMA work hides (fitted on
+    // sweeps of forced splits at H=64, BF16 and FP8 rows, K = 512 .. 2048,
+    // T = 1 .. 512).
+    const int64_t row_w = (H == 64 && kv_dtype == SMLA_DTYPE_BF16) ? 1 : 2;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {
       const int64_t cps = (num_chunks + s - 1) / s;

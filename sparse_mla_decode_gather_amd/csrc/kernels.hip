@@ -12,8 +12,7 @@
 //
 // Kernel design (ours, for CDNA4; the pages' TRTLLM-gen / CuTe kernels are
 // prior art only):
-//  * One workgroup of 4 wave64s (2 at H=64 with FP8 or packed rows) per
-//    (token, split), one wave per SIMD.  All H heads of the token live in the workgroup, so each gathered
+//  * One workgroup of 4 wave64s per (token, split), one wave per SIMD.  All H heads of the token live in the workgroup, so each gathered
 //    row is read from HBM once per (token, split) and reused by every head.
 //  * The split's table columns are compacted first (masked, -1, truncated
 //    and out-of-range slots are dropped), so tiles are dense.
@@ -32,12 +31,11 @@
 //    first tile and left alone; a tile exceeding it by more than 2^64 makes
 //    the split start over with the higher reference, so O is never rescaled
 //    and the result is exact up to rounding.
-//  * decode_kernel (H=64, FP8 or packed rows): wave w computes S and O for
-//    its own 32 heads.  decode_hd_kernel (H=128): wave w computes S for 32
-//    heads but O for a quarter of the output dims of all heads, with P
-//    exchanged through LDS (see there).  decode_h64_kernel (H=64, BF16 q
-//    and rows): the same split of O over four waves, with S of a 64-row
-//    tile split over the waves by head block and row block.  FP8 q and FP8 rows are widened exactly to BF16 and
+//  * decode_hd_kernel (H=128): wave w computes S for 32 heads but O for a
+//    quarter of the output dims of all heads, with P exchanged through LDS
+//    (see there).  decode_h64_kernel (H=64): the same split of O over four
+//    waves, with S of a 64-row tile split over the waves by head block and
+//    row block.  FP8 q and FP8 rows are widened exactly to BF16 and
 //    multiplied on the BF16 MFMA.
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
@@ -56,7 +54,6 @@ namespace {
 
 constexpr int kD = kHeadDim;
 constexpr int kTile = 32;          // rows per LDS tile
-constexpr int kSeg = 2048;         // table columns compacted per pass
 constexpr int kRowBytes = kD * 2;  // a BF16 row
 // LDS row pitch: a BF16 row plus 48 B of padding (pitch = 48 mod 256).
 // 16 lanes reading the same 16-B chunk of 16 consecutive rows then hit 16
@@ -461,408 +458,12 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
   return 8 * (i >> 2) + 4 * kg + (i & 3);
 }
 
-// SERIAL (a check for LDS races, not a production path): every step of the
-// tile pipeline completes, row loads included, and all waves meet at a
-// barrier before the next step starts, so no two steps overlap.  The
-// arithmetic is the same instruction for instruction, so a pipelined call
-// must give the same bits; a difference exposes a race between the steps.
-template <int NW, bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false,
-          bool SERIAL = false>
-__global__ __launch_bounds__(NW * 64, 1)
-void decode_kernel(DecodeParams p) {
-  static_assert(KV_FP8, "FP8 or packed rows (BF16 rows: decode_h64_kernel)");
-  static_assert(!PACKED || !Q_FP8, "packed rows: BF16 q");
-  // all loads of the wave landed and every wave arrived (SERIAL only)
-  auto serial_point = [](bool wait_loads) {
-    if constexpr (SERIAL) {
-      if (wait_loads) wait_vmcnt<0>();
-      __syncthreads();
-    }
-  };
-  constexpr int H = NW * 32;              // one wave per 32 heads
-  constexpr int NT = NW * 64;
-  constexpr int RPW = kTile / NW;         // tile rows each wave gathers
-  // Row gather into NSTAGE LDS tiles through registers (8 bytes of an FP8
-  // row per lane, 16 of a packed row), widened to BF16 on the way.  The
-  // loads for tile it+NSTAGE-1 are in flight while tile it is computed.
-  constexpr int NSTAGE = 2;
-  __shared__ __attribute__((aligned(16))) uint8_t kv_lds[NSTAGE * kTileBytes];
-  __shared__ __attribute__((aligned(16))) int32_t slots[kSeg];
-  __shared__ int32_t wave_cnt[NW];
-  __shared__ int32_t restart_flag;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // in an SGPR
-  const int l32 = lane & 31;
-  const int kg = lane >> 5;
-
-  // XCD-aware mapping: the hardware hands consecutive workgroup ids to the
-  // 8 XCDs round-robin, so give each XCD a contiguous range of work items;
-  // the splits of one token and neighbouring tokens (which share rows in
-  // speculative decode) then run together on one XCD and share its L2.
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int q8 = nblk >> 3, r8 = nblk & 7;
-  const int item = xcd * q8 + min(xcd, r8) + (blockIdx.x >> 3);
-  const int t = item / p.S;
-  const int s = item - t * p.S;
-  const int head = wave * 32 + l32;
-
-  TokenTable<GEN> tt = token_table<GEN>(p, t);
-  int len_a, len_b;
-  token_length_loads<GEN>(p, t, len_a, len_b);
-  // The first compaction pass's table entries go out with the lengths and
-  // before Q, so that their latency overlaps Q's instead of following it
-  // (columns past the token's length are loaded too and dropped in the
-  // compaction).
-  const int c_begin = s * p.split_cols;
-  int r_first = -1;
-  if (c_begin + (int)threadIdx.x < min(p.K, c_begin + p.split_cols))
-    r_first = tt.raw(p, c_begin + threadIdx.x);
-  const bool lens_ok = token_lengths<GEN>(p, len_a, len_b, tt);
-  if (p.validate && threadIdx.x == 0 && s == 0 && !lens_ok) record_error(p.err, 2, t, -1);
-  const int c_end = min(tt.end(), c_begin + p.split_cols);
-
-  // Q^T fragments (B operand of S^T = K Q^T): lane holds head `head`,
-  // dims [16kk + 8kg, +8) for each 16-dim step kk.
-  bf16x8 qf[32];
-  {
-    const size_t qrow = ((size_t)t * H + head) * kD;
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-      const int d0 = kk * 16 + kg * 8;
-      u32x4 v;
-      if constexpr (Q_FP8)
-        v = widen_e4m3fn_x8(*(const u32x2*)((const uint8_t*)p.q + qrow + d0));
-      else
-        v = *(const u32x4*)((const uint16_t*)p.q + qrow + d0);
-      qf[kk] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // Drain the Q loads here: otherwise their waits land inside the tile
-  // loop, where vmcnt also counts the row gathers in flight.
-  wait_vmcnt<0>();
-
-  float m_run = -INFINITY;   // reference max (base-2 logits) of head `head`
-  float l_run = 0.f;         // this lane's share of the normaliser
-  f32x16 o[16];              // O^T: d-block db, d = 32db + 8(i/4) + 4kg + i%4
-#pragma unroll
-  for (int db = 0; db < 16; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-
-  // per-lane LDS offsets inside a tile
-  const int qk_off = l32 * kRowPitch + kg * 16;
-  const int i16 = lane & 15, grp = lane >> 4;
-  const int tr_off = (4 * (grp >> 1) + (i16 >> 2)) * kRowPitch +
-                     (16 * (grp & 1) + 4 * (i16 & 3)) * 2;
-
-  if (threadIdx.x == 0) restart_flag = 0;
-  // A per-lane sticky flag: some tile outgrew the reference max by more
-  // than kRefSlack (m_run has then been raised to that tile's max).  It is
-  // checked once per segment; tiles processed after it are discarded by the
-  // restart, and one restart always suffices since m_run only grows.
-  bool need_sticky = false;
-
-  // ---- the three phases of a 32-row tile ------------------------------------
-  // S^T for a tile (raw logits, before bmm1_scale).
-  // The MFMA operand reads run kLead steps ahead of the MFMAs; the order is
-  // pinned with scheduling barriers (the compiler then counts the LDS reads
-  // in flight and waits for exactly the one each MFMA needs).
-  constexpr int kLead = 4;
-  auto qk = [&](const uint8_t* tb, auto&& every4) -> f32x16 {
-    bf16x8 a[kLead];
-#pragma unroll
-    for (int k = 0; k < kLead; ++k) a[k] = *(const bf16x8*)(tb + qk_off + k * 32);
-    f32x16 acc;
-#pragma unroll
-    for (int kk = 0; kk < 32; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk == 0) acc = mfma_qk_first(a[0], qf[0]);
-      else mfma_qk(acc, a[kk % kLead], qf[kk]);
-      if (kk + kLead < 32)
-        a[kk % kLead] = *(const bf16x8*)(tb + qk_off + (kk + kLead) * 32);
-      if ((kk & 3) == 3) {
-        __builtin_amdgcn_sched_barrier(0);
-        every4(kk >> 2);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    return acc;
-  };
-
-  // Online softmax of one tile's S^T; returns P^T as the two B operands of
-  // the PV steps.  Rows past n_tile (a ragged last tile) repeat the tile's
-  // last active row: they cannot raise the max and get probability 0.
-  auto softmax = [&](f32x16 sv, int n_tile, bf16x8 (&pf)[2], auto full) {
-    constexpr bool kFull = decltype(full)::value;   // n_tile == kTile known
-    mfma_qk_drain(sv);
-    float smax = sv[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
-    smax = max_with_other_half(smax);
-    const float tmax = smax * p.scale_log2;       // scale_log2 > 0
-    // The reference max is set by the first tile and then left alone, so O
-    // is never rescaled inside the loop.
-    m_run = (m_run == -INFINITY) ? tmax : m_run;
-    const bool need = tmax > m_run + kRefSlack;
-    m_run = need ? tmax : m_run;
-    need_sticky |= need;
-    const float neg_m = -m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 pk;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i0 = 8 * h + 2 * k;
-        float p0 = fast_exp2(__builtin_fmaf(sv[i0], p.scale_log2, neg_m));
-        float p1 = fast_exp2(__builtin_fmaf(sv[i0 + 1], p.scale_log2, neg_m));
-        if (!kFull && n_tile < kTile) {   // wave-uniform; only a ragged last tile
-          p0 = (tile_row_of_reg(i0, kg) < n_tile) ? p0 : 0.f;
-          p1 = (tile_row_of_reg(i0 + 1, kg) < n_tile) ? p1 : 0.f;
-        }
-        lsum += p0 + p1;
-        pk[k] = pack_bf16x2(p0, p1);
-      }
-      pf[h] = __builtin_bit_cast(bf16x8, pk);
-    }
-    l_run += lsum;
-  };
-  // O^T += V^T P^T for a tile: step k covers rows [16h, 16h+16) (h = k/16)
-  // of d-block db = k%16.
-  // O^T += V^T P^T for the tile at tb; `every(k)` runs after MFMA k.
-  auto pv = [&](const uint8_t* tb, const bf16x8 (&pf)[2], auto&& every) {
-    auto vfrag = [&](int k) -> bf16x8 {
-      const uint8_t* vb = tb + tr_off + (16 * (k >> 4)) * kRowPitch + (k & 15) * 64;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 __attribute__((address_space(3)))*)(vb));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (s16x4 __attribute__((address_space(3)))*)(vb + 8 * kRowPitch));
-      return __builtin_bit_cast(bf16x8,
-                                __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    bf16x8 v[kLead];
-#pragma unroll
-    for (int k = 0; k < kLead; ++k) v[k] = vfrag(k);
-#pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      __builtin_amdgcn_sched_barrier(0);
-      o[k & 15] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v[k % kLead], pf[k >> 4],
-                                                         o[k & 15], 0, 0, 0);
-      if (k + kLead < 32) v[k % kLead] = vfrag(k + kLead);
-      every(k);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto pv_no_hook = [](int) {};
-
-  bool again;
-  do {
-  again = false;
-  for (int seg0 = c_begin; seg0 < c_end && !again; seg0 += kSeg) {
-    const int seg1 = min(c_end, seg0 + kSeg);
-
-    // ---- compact the active slots of this segment into LDS ----------------
-    __syncthreads();   // the previous segment no longer reads slots[] / tiles
-    int n_act = 0;
-    for (int c0 = seg0; c0 < seg1; c0 += NT) {
-      const int c = c0 + threadIdx.x;
-      bool act = false;
-      int code = 0;
-      if (c < seg1 && tt.live(c)) {
-        const int r = (c0 == c_begin) ? r_first : tt.raw(p, c);
-        if (r != -1) {
-          const bool swa = tt.swa(c);
-          const int64_t rows = swa ? p.swa_rows : p.comp_rows;
-          if (r >= 0 && (int64_t)r < rows) {
-            act = true;
-            code = swa ? r : (int)((uint32_t)r | 0x80000000u);
-          } else if (p.validate) {
-            record_error(p.err, 1, t, c);
-          }
-        }
-      }
-      const uint64_t bal = __ballot(act);
-      const int pre = __popcll(bal & ((1ull << lane) - 1ull));
-      if (lane == 0) wave_cnt[wave] = __popcll(bal);
-      __syncthreads();
-      int off = n_act, tot = 0;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) {
-        const int cw = wave_cnt[w2];
-        off += (w2 < wave) ? cw : 0;
-        tot += cw;
-      }
-      if (act) slots[off + pre] = code;
-      n_act += tot;
-      __syncthreads();
-    }
-    const int ntiles = (n_act + kTile - 1) / kTile;
-    auto n_in = [&](int tile) { return min(kTile, n_act - tile * kTile); };
-
-    // Row j of a tile is slot tile*32 + j; the ragged tail of the last tile
-    // repeats the last active row.  Slot codes are wave-uniform: they are
-    // read into SGPRs and row addresses are computed on the scalar unit.
-    auto stage = [&](int tile) -> const uint8_t* {
-      return kv_lds + (tile % NSTAGE) * kTileBytes;
-    };
-
-    // Register-staged gather of FP8 rows: lane `lane` carries 8 B of a row,
-    // widened to BF16 when written to LDS.  The loads of tile it+NSTAGE-1
-    // are issued while the S^T MFMAs of tile it run and written to LDS
-    // after its O^T MFMAs, into the stage tile it-1 used.
-    constexpr int VW = 2;                       // dwords per lane per row
-    typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
-    // (The rows' addresses here come from a scalar chain per row rather
-    // than from one VALU pass read out per row, as in the LDS-DMA kernels:
-    // with the loads' registers live, the readouts' VALU-to-SGPR waits
-    // cost more than they save; measured 7-10% slower on FP8 and packed
-    // rows.)
-    const int last_code = __builtin_amdgcn_readfirstlane(slots[max(n_act - 1, 0)]);
-    const uint32_t lane_off = (uint32_t)lane * (VW * 4);
-    const PackedLane pl = packed_lane(lane);   // packed rows only
-    stage_t st[RPW];
-    auto fetch_codes = [&](int tile, int (&codes)[RPW]) {
-      const int s0 = tile * kTile + wave_u * RPW;
-#pragma unroll
-      for (int q = 0; q < RPW / 4; ++q) {
-        const u32x4 c4 = *(const u32x4*)(slots + s0 + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) codes[4 * q + e] = (int)c4[e];
-      }
-    };
-    auto load_row = [&](int tile, int jj, const int (&codes)[RPW]) {
-      const int s0 = tile * kTile + wave_u * RPW;
-      int code = __builtin_amdgcn_readfirstlane(codes[jj]);
-      code = (s0 + jj < n_act) ? code : last_code;
-      const uint8_t* base = code < 0 ? p.comp : p.swa;
-      const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
-      if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
-      else st[jj] = load_row8(row, lane_off);
-    };
-    auto store_row = [&](int tile, int jj) {
-      uint8_t* dst = kv_lds + (tile % NSTAGE) * kTileBytes;
-      if constexpr (PACKED) {
-        *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
-            packed_tile_bytes(st[jj], pl);
-      } else {
-        *(u32x4*)(dst + (wave_u * RPW + jj) * kRowPitch + lane * 16) =
-            widen_e4m3fn_x8(st[jj]);
-      }
-    };
-    auto store = [&](int tile) {
-#pragma unroll
-      for (int jj = 0; jj < RPW; ++jj) store_row(tile, jj);
-    };
-    // prologue: tiles 0 .. NSTAGE-2 into their stages
-    for (int tl = 0; tl < min(NSTAGE - 1, ntiles); ++tl) {
-      int codes[RPW];
-      fetch_codes(tl, codes);
-#pragma unroll
-      for (int jj = 0; jj < RPW; ++jj) load_row(tl, jj, codes);
-      store(tl);
-    }
-    // STEADY iterations (the next tile is loaded, tile it is whole) are a
-    // compile-time variant with no branches in their body.
-    auto iteration = [&](auto steady, int it) {
-      constexpr bool kSteady = decltype(steady)::value;
-      __syncthreads();            // tile it stored by every wave; it-1 done
-      const int nxt = it + NSTAGE - 1;
-      const bool do_load = kSteady || nxt < ntiles;
-      int codes[RPW];
-      fetch_codes(do_load ? nxt : it, codes);
-      const f32x16 sv = qk(stage(it), [&](int q) {
-#pragma unroll
-        for (int r = 0; r < RPW / 8; ++r)
-          if (do_load) load_row(nxt, q * (RPW / 8) + r, codes);
-      });
-      serial_point(true);
-      bf16x8 pf[2];
-      softmax(sv, n_in(it), pf, steady);
-      if constexpr (kSteady) {
-        // The next tile's rows go to its stage (the one tile it-1 used,
-        // free since the barrier) between the O^T MFMAs, one row per two
-        // MFMAs: their loads went out during the S^T MFMAs.
-        static_assert(2 * RPW <= 32, "a row per two O^T MFMAs");
-        pv(stage(it), pf, [&](int k) {
-          if ((k & 1) == 0 && (k >> 1) < RPW) store_row(nxt, k >> 1);
-        });
-      } else {
-        pv(stage(it), pf, pv_no_hook);
-        if (do_load) store(nxt);
-      }
-      serial_point(false);
-    };
-    int it = 0;
-    for (; it + NSTAGE - 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
-    for (; it < ntiles; ++it) iteration(BoolC<false>{}, it);
-    // did any wave's tile outgrow its reference max?
-    if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
-    __syncthreads();
-    again = restart_flag != 0;
-  }
-  if (again) {
-    // Rare: start the split over with the raised reference maxima.
-    wait_vmcnt<0>();                // no row gather may still be landing
-    __syncthreads();
-    if (threadIdx.x == 0) restart_flag = 0;
-    need_sticky = false;
-    l_run = 0.f;
-#pragma unroll
-    for (int db = 0; db < 16; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
-  }
-  } while (again);
-
-  // ---- epilogue ------------------------------------------------------------
-  float l = l_run + __shfl_xor(l_run, 32);
-  float m = m_run;
-  float inv, lse;
-  if constexpr (SPLIT) {
-    inv = (l > 0.f) ? p.bmm2 / l : 0.f;
-    lse = (l > 0.f) ? m + fast_log2(l) : -INFINITY;
-  } else {
-    float fac = 1.f;
-    if (p.sinks) {
-      const float sl = p.sinks[head] * kLog2e;
-      const float mm = fmaxf(m, sl);
-      fac = fast_exp2(m - mm);       // 0 when nothing was active (m = -inf)
-      l = l * fac + fast_exp2(sl - mm);
-      m = mm;
-    }
-    inv = (l > 0.f) ? fac * p.bmm2 / l : 0.f;
-    lse = (l > 0.f) ? p.lse_scale * (m + fast_log2(l)) : -INFINITY;
-  }
-  uint16_t* dst;
-  if constexpr (SPLIT)
-    dst = p.mid_out + (((size_t)t * H + head) * p.S + s) * kD;
-  else
-    dst = (uint16_t*)p.out + ((size_t)t * H + head) * kD;
-#pragma unroll
-  for (int db = 0; db < 16; ++db) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      u32x2 w;
-      w[0] = pack_bf16x2(o[db][4 * a] * inv, o[db][4 * a + 1] * inv);
-      w[1] = pack_bf16x2(o[db][4 * a + 2] * inv, o[db][4 * a + 3] * inv);
-      *(u32x2*)(dst + db * 32 + a * 8 + kg * 4) = w;
-    }
-  }
-  if (kg == 0) {
-    if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
-    else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // split kernel, H = 128 with BF16 rows: heads for S, output dims for O
 // ---------------------------------------------------------------------------
 //
 // Four waves.  Wave w computes S^T and the softmax of heads [32w, 32w+32)
-// (a 32 x 32 S^T tile per 32-row KV tile, as above), but accumulates O^T
+// (a 32 x 32 S^T tile per 32-row KV tile), but accumulates O^T
 // for the output dims [128w, 128w+128) of all 128 heads.  P^T is exchanged
 // through LDS in exactly the B-operand layout the O^T MFMAs take, so the
 // exchange is one 16-byte store and one 16-byte load per lane and head
@@ -882,7 +483,11 @@ void decode_kernel(DecodeParams p) {
 // BF16 rows go by LDS-DMA.  GATHER_ONLY: the same compaction and BF16 row gather
 // with no arithmetic and no output (a measurement aid: the attainable
 // gather rate on the same tables).
-// SERIAL: the LDS-race check of decode_kernel (see there) for this kernel.
+// SERIAL (a check for LDS races, not a production path): every step of the
+// tile pipeline completes, row loads included, and all waves meet at a
+// barrier before the next step starts, so no two steps overlap.  The
+// arithmetic is the same instruction for instruction, so a pipelined call
+// must give the same bits; a difference exposes a race between the steps.
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GATHER_ONLY = false, bool GEN = false,
           bool STREAM = false, bool PACKED = false, bool SERIAL = false>
 __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
@@ -917,9 +522,12 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   const int l32 = lane & 31;
   const int kg = lane >> 5;
 
-  // XCD-aware work mapping (see decode_kernel): XCD x owns the contiguous
-  // item range [lo, lo + cnt) and starts its workgroups in the order of
-  // blockIdx.x >> 3.  With per-token lengths, and more items than CUs (the
+  // XCD-aware work mapping: the hardware hands consecutive workgroup ids to
+  // the 8 XCDs round-robin, so each XCD gets a contiguous range of work
+  // items; the splits of one token and neighbouring tokens (which share rows
+  // in speculative decode) then run together on one XCD and share its L2.
+  // XCD x owns the item range [lo, lo + cnt) and starts its workgroups in
+  // the order of blockIdx.x >> 3.  With per-token lengths, and more items than CUs (the
   // host sets rank_items; with one item per CU the order cannot matter and
   // the ranking would only put a dependent load in front of every item's
   // own loads), the items of the range are started longest first (rank by active columns of the item's split, ties
@@ -1130,7 +738,10 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
         smax = max_with_other_half(smax);
       } else if (k == 2) {
         // The reference max is set by the first tile and then left alone,
-        // so O is never rescaled inside the loop (see decode_kernel).
+        // so O is never rescaled inside the loop; a tile that outgrows it
+        // by more than kRefSlack raises it and sets the sticky flag, and
+        // the split restarts once with the raised reference (it only
+        // grows, so one restart suffices).
         tmax = smax * p.scale_log2;     // scale_log2 > 0
         m_run = (m_run == -INFINITY) ? tmax : m_run;
         need = tmax > m_run + kRefSlack;
@@ -1589,23 +1200,28 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 }
 
 // ---------------------------------------------------------------------------
-// split kernel, H = 64 with BF16 rows: four waves, 64-row tiles
+// split kernel, H = 64: four waves, 64-row tiles
 // ---------------------------------------------------------------------------
 //
-// decode_kernel gives each of its two waves 32 heads for both products, so
-// two workgroups share a CU and every wave reads the whole V tile.  Here one
-// workgroup of four waves fills the CU: wave w computes S^T and the softmax
-// of heads [32(w&1), +32) over rows [32(w>>1), +32) of a 64-row tile, and
-// O^T for the output dims [128w, +128) of all 64 heads over all 64 rows, with
-// P^T exchanged through LDS in the O^T MFMAs' B-operand layout (as in
-// decode_hd_kernel).  Two LDS stages of 64 rows: the rows of tile i+1 go out
-// by LDS-DMA during the S^T MFMAs of tile i.  The two waves that share a
+// One workgroup of four waves fills the CU: wave w computes S^T and the
+// softmax of heads [32(w&1), +32) over rows [32(w>>1), +32) of a 64-row
+// tile, and O^T for the output dims [128w, +128) of all 64 heads over all 64
+// rows, with P^T exchanged through LDS in the O^T MFMAs' B-operand layout
+// (as in decode_hd_kernel).  (Two workgroups of two waves, each wave
+// holding 32 heads of O for all 512 dims, would make every wave read the
+// whole tile for both products: a third more LDS reads per row.)  Two LDS stages of 64 rows: the rows of tile i+1 go out
+// during the S^T MFMAs of tile i, by LDS-DMA (BF16 rows) or into registers
+// (FP8 and packed rows; widened and written to their stage between the O^T
+// MFMAs of tile i, the stage tile i-1 used).  The two waves that share a
 // head block share its reference max: the first tile's is the max over both
 // row blocks (exchanged through LDS), and a restart takes the larger of the
 // two waves' raised maxima.  The normaliser adds the two waves' sums.
-template <bool SPLIT, bool GEN, bool SERIAL = false>
+template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false,
+          bool SERIAL = false>
 __global__ __launch_bounds__(256, 1)
 void decode_h64_kernel(DecodeParams p) {
+  static_assert(!PACKED || (KV_FP8 && !Q_FP8), "packed rows: BF16 q, register-staged rows");
+  static_assert(!Q_FP8 || KV_FP8, "FP8 q needs FP8 rows");
   constexpr int NW = 4, H = 64, NT = 256;
   constexpr int TR = 64;                  // tile rows
   constexpr int RPW = TR / NW;            // rows each wave gathers per tile
@@ -1701,8 +1317,12 @@ void decode_h64_kernel(DecodeParams p) {
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) {
       const int d0 = kk * 16 + kg * 8;
-      qf[kk] = __builtin_bit_cast(
-          bf16x8, *(const global_u32x4*)((const uint16_t*)p.q + qrow + d0));
+      u32x4 v;
+      if constexpr (Q_FP8)
+        v = widen_e4m3fn_x8(load_global8((const uint8_t*)p.q + qrow, d0));
+      else
+        v = *(const global_u32x4*)((const uint16_t*)p.q + qrow + d0);
+      qf[kk] = __builtin_bit_cast(bf16x8, v);
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -1768,8 +1388,9 @@ void decode_h64_kernel(DecodeParams p) {
   };
   // O^T += V^T P^T over the tile's 64 rows.  MFMA k: 16-row step h = k/8,
   // dim block db = (k/2) % 4, head block hb = k % 2; V^T fragment f = 4h + db
-  // is read two fragments ahead, P^T of step h+1 during step h.
-  auto ot = [&](const uint8_t* vt) {
+  // is read two fragments ahead, P^T of step h+1 during step h.  hook(k)
+  // runs after MFMA k.
+  auto ot = [&](const uint8_t* vt, auto&& hook) {
     bf16x8 v[3], pf[2][NHB];
     pf[0][0] = pfrag(0, 0);
     pf[0][1] = pfrag(0, 1);
@@ -1786,9 +1407,48 @@ void decode_h64_kernel(DecodeParams p) {
         pf[(h + 1) & 1][0] = pfrag(h + 1, 0);
         pf[(h + 1) & 1][1] = pfrag(h + 1, 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      hook(k);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
+  // The softmax of this wave's 32 rows of a tile with nt valid rows (rows
+  // past nt get probability 0), P^T to LDS.
+  auto softmax_pt = [&](f32x16 sv, int nt) {
+    if (nt < TR) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        sv[i] = (rbs * 32 + tile_row_of_reg(i, kg) < nt) ? sv[i] : -INFINITY;
+    }
+    float smax = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
+#pragma unroll
+    for (int i = 3; i < 15; i += 2) smax = fmaxf(fmaxf(smax, sv[i]), sv[i + 1]);
+    smax = max_with_other_half(fmaxf(smax, sv[15]));
+    float tmax = smax * p.scale_log2;          // scale_log2 > 0
+    if (!ref_set) {
+      // the first tile: the reference is the max over both row blocks
+      if (kg == 0) pair_lds[rbs][head] = tmax;
+      __syncthreads();
+      m_run = fmaxf(pair_lds[0][head], pair_lds[1][head]);
+      ref_set = true;
+    }
+    const bool need = tmax > m_run + kRefSlack;
+    m_run = need ? tmax : m_run;
+    need_sticky |= need;
+    float lsum = 0.f;
+    u32x4 pk[2];
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+      const float p0 = fast_exp2(__builtin_fmaf(sv[j], p.scale_log2, -m_run));
+      const float p1 = fast_exp2(__builtin_fmaf(sv[j + 1], p.scale_log2, -m_run));
+      lsum += p0 + p1;
+      pk[j >> 3][(j & 7) >> 1] = pack_bf16x2(p0, p1);
+    }
+    l_run += lsum;
+    p_lds[(hbs * NKS + 2 * rbs + 0) * 64 + lane] = pk[0];
+    p_lds[(hbs * NKS + 2 * rbs + 1) * 64 + lane] = pk[1];
+  };
+  auto no_hook = [](int) {};
 
   bool again;
   bool first_seg = true;
@@ -1847,10 +1507,11 @@ void decode_h64_kernel(DecodeParams p) {
       for (int i = n_act; i < ntiles * TR; ++i) slots[i] = last;
     }
     __syncthreads();
+    auto stage = [&](int tile) -> const uint8_t* {
+      return kv_lds + (tile % NSTAGE) * kStageBytes;
+    };
+    if constexpr (!KV_FP8) {
     if (ntiles > 0) {
-      auto stage = [&](int tile) -> const uint8_t* {
-        return kv_lds + (tile % NSTAGE) * kStageBytes;
-      };
       // lane j < RPW: the address of this wave's row j of `tile`
       auto lane_row_addr = [&](int tile) -> uint64_t {
         const int code = slots[tile * TR + wave_u * RPW + (lane & (RPW - 1))];
@@ -1896,45 +1557,87 @@ void decode_h64_kernel(DecodeParams p) {
           }
         });
         mfma_qk_drain(sv);
-        const int nt = min(TR, n_act - it * TR);
-        if (nt < TR) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            sv[i] = (rbs * 32 + tile_row_of_reg(i, kg) < nt) ? sv[i] : -INFINITY;
-        }
         serial_point(true);
-        // ---- softmax of this wave's 32 rows ---------------------------------
-        float smax = fmaxf(fmaxf(sv[0], sv[1]), sv[2]);
-#pragma unroll
-        for (int i = 3; i < 15; i += 2) smax = fmaxf(fmaxf(smax, sv[i]), sv[i + 1]);
-        smax = max_with_other_half(fmaxf(smax, sv[15]));
-        float tmax = smax * p.scale_log2;          // scale_log2 > 0
-        if (!ref_set) {
-          // the first tile: the reference is the max over both row blocks
-          if (kg == 0) pair_lds[rbs][head] = tmax;
-          __syncthreads();
-          m_run = fmaxf(pair_lds[0][head], pair_lds[1][head]);
-          ref_set = true;
-        }
-        const bool need = tmax > m_run + kRefSlack;
-        m_run = need ? tmax : m_run;
-        need_sticky |= need;
-        float lsum = 0.f;
-        u32x4 pk[2];
-#pragma unroll
-        for (int j = 0; j < 16; j += 2) {
-          const float p0 = fast_exp2(__builtin_fmaf(sv[j], p.scale_log2, -m_run));
-          const float p1 = fast_exp2(__builtin_fmaf(sv[j + 1], p.scale_log2, -m_run));
-          lsum += p0 + p1;
-          pk[j >> 3][(j & 7) >> 1] = pack_bf16x2(p0, p1);
-        }
-        l_run += lsum;
-        p_lds[(hbs * NKS + 2 * rbs + 0) * 64 + lane] = pk[0];
-        p_lds[(hbs * NKS + 2 * rbs + 1) * 64 + lane] = pk[1];
+        softmax_pt(sv, min(TR, n_act - it * TR));
         __syncthreads();                // P^T of tile it published
-        ot(stage(it));
+        ot(stage(it), no_hook);
         serial_point(false);
       }
+    }
+    } else {
+    if (ntiles > 0) {
+      // FP8 and packed rows through registers: each lane holds 8 bytes of
+      // an FP8 row (16 of a packed row) for each of the wave's RPW rows of
+      // the next tile.  Row addresses come from a scalar chain per row
+      // (with the loads' registers live, reading one VALU pass out per row
+      // costs more than it saves).  These are ordinary loads, so the compiler's
+      // own waits before the stores are exact.
+      typedef std::conditional_t<PACKED, u32x4, u32x2> stage_t;
+      stage_t st[RPW];
+      const uint32_t lane_off8 = (uint32_t)lane * 8u;
+      const PackedLane pl = packed_lane(lane);   // packed rows only
+      // the slot codes of rows jj, jj+1 of this wave's rows of `tile`
+      auto fetch_codes = [&](int tile, int jj) -> u32x2 {
+        return *(const u32x2*)(slots + tile * TR + wave_u * RPW + jj);
+      };
+      auto load_row = [&](int jj, uint32_t raw) {
+        const int code = __builtin_amdgcn_readfirstlane((int)raw);
+        const uint8_t* base = code < 0 ? p.comp : p.swa;
+        const uint8_t* row = base + (int64_t)(code & 0x7FFFFFFF) * p.row_stride_bytes;
+        if constexpr (PACKED) st[jj] = packed_load_row(row, pl);
+        else st[jj] = load_row8(row, lane_off8);
+      };
+      auto store_row = [&](int tile, int jj) {
+        uint8_t* dst = kv_lds + (tile % NSTAGE) * kStageBytes +
+                       (wave_u * RPW + jj) * kRowPitch + lane * 16;
+        if constexpr (PACKED) *(u32x4*)dst = packed_tile_bytes(st[jj], pl);
+        else *(u32x4*)dst = widen_e4m3fn_x8(st[jj]);
+      };
+      {
+#pragma unroll
+        for (int jj = 0; jj < RPW; jj += 2) {
+          const u32x2 c = fetch_codes(0, jj);
+          load_row(jj, c[0]);
+          load_row(jj + 1, c[1]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < RPW; ++jj) store_row(0, jj);
+      }
+      // STEADY iterations (a next tile exists) are a compile-time variant,
+      // so that no branch sits between the loads and their stores (at a
+      // branch merge the compiler would wait for every load).
+      auto iteration = [&](auto steady, int it) {
+        constexpr bool kSteady = decltype(steady)::value;
+        __syncthreads();                // tile it stored by every wave; O^T of it-1 done
+        // two rows per four S^T MFMAs, their codes read at the hook before
+        static_assert(RPW == 16, "two rows per hook");
+        u32x2 codes = {0u, 0u};
+        if constexpr (kSteady) codes = fetch_codes(it + 1, 0);
+        f32x16 sv = qk(stage(it), [&](int q) {
+          if constexpr (kSteady) {
+            load_row(2 * q, codes[0]);
+            load_row(2 * q + 1, codes[1]);
+            if (q + 1 < 8) codes = fetch_codes(it + 1, 2 * q + 2);
+          }
+        });
+        mfma_qk_drain(sv);
+        serial_point(true);
+        softmax_pt(sv, min(TR, n_act - it * TR));
+        __syncthreads();                // P^T of tile it published
+        // the next tile's rows go to its stage (free since the first
+        // barrier), one row per two O^T MFMAs
+        static_assert(2 * RPW <= 32, "a row per two O^T MFMAs");
+        ot(stage(it), [&](int k) {
+          if constexpr (kSteady) {
+            if ((k & 1) == 0 && (k >> 1) < RPW) store_row(it + 1, k >> 1);
+          }
+        });
+        serial_point(false);
+      };
+      int it = 0;
+      for (; it + 1 < ntiles; ++it) iteration(BoolC<true>{}, it);
+      iteration(BoolC<false>{}, it);
+    }
     }
     if (__ballot(need_sticky) != 0ull && lane == 0) restart_flag = 1;
     __syncthreads();
@@ -2264,52 +1967,29 @@ hipError_t launch_decode_hd_packed(const DecodeParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// BF16 q and rows at H = 64: the four-wave kernel.
+// H = 64: the four-wave kernel.
+template <bool QF, bool KF, bool PK = false>
 hipError_t launch_decode_h64(const DecodeParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)(p.T * p.S));
   const bool gen = p.segmented != 0;
   if (p.serial) {            // combined table only (checked on the host)
     if (gen) return hipErrorInvalidValue;
     if (p.S > 1)
-      hipLaunchKernelGGL((decode_h64_kernel<true, false, true>), grid, dim3(256), 0, stream, p);
-    else
-      hipLaunchKernelGGL((decode_h64_kernel<false, false, true>), grid, dim3(256), 0, stream, p);
-    return hipGetLastError();
-  }
-  if (p.S > 1 && gen)
-    hipLaunchKernelGGL((decode_h64_kernel<true, true>), grid, dim3(256), 0, stream, p);
-  else if (p.S > 1)
-    hipLaunchKernelGGL((decode_h64_kernel<true, false>), grid, dim3(256), 0, stream, p);
-  else if (gen)
-    hipLaunchKernelGGL((decode_h64_kernel<false, true>), grid, dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_h64_kernel<false, false>), grid, dim3(256), 0, stream, p);
-  return hipGetLastError();
-}
-
-template <int NW, bool QF, bool KF, bool PK = false>
-hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)(p.T * p.S));
-  const dim3 block(NW * 64);
-  const bool gen = p.segmented != 0;
-  if (p.serial) {
-    if (gen) return hipErrorInvalidValue;
-    if (p.S > 1)
-      hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false, PK, true>), grid, block, 0,
+      hipLaunchKernelGGL((decode_h64_kernel<QF, KF, true, false, PK, true>), grid, dim3(256), 0,
                          stream, p);
     else
-      hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false, PK, true>), grid, block, 0,
+      hipLaunchKernelGGL((decode_h64_kernel<QF, KF, false, false, PK, true>), grid, dim3(256), 0,
                          stream, p);
     return hipGetLastError();
   }
   if (p.S > 1 && gen)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, true, PK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_h64_kernel<QF, KF, true, true, PK>), grid, dim3(256), 0, stream, p);
   else if (p.S > 1)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, true, false, PK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_h64_kernel<QF, KF, true, false, PK>), grid, dim3(256), 0, stream, p);
   else if (gen)
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, true, PK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_h64_kernel<QF, KF, false, true, PK>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<NW, QF, KF, false, false, PK>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((decode_h64_kernel<QF, KF, false, false, PK>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -2355,14 +2035,14 @@ hipError_t launch_decode(const DecodeParams& p, int q_dtype, int kv_dtype,
                          hipStream_t stream) {
   if (kv_dtype == kKvPacked584) {        // BF16 q only (checked on the host)
     if (q_dtype != 0) return hipErrorInvalidValue;
-    if (p.H == 64) return launch_decode_t<2, false, true, true>(p, stream);
+    if (p.H == 64) return launch_decode_h64<false, true, true>(p, stream);
     return launch_decode_hd_packed(p, stream);
   }
   const bool qf = q_dtype != 0, kf = kv_dtype != 0;
   if (p.H == 64) {
-    if (!qf && !kf) return launch_decode_h64(p, stream);
-    if (qf && kf) return launch_decode_t<2, true, true>(p, stream);
-    return launch_decode_t<2, false, true>(p, stream);
+    if (!qf && !kf) return launch_decode_h64<false, false>(p, stream);
+    if (qf && kf) return launch_decode_h64<true, true>(p, stream);
+    return launch_decode_h64<false, true>(p, stream);
   }
   if (!kf) return launch_decode_hd<false, false>(p, stream);   // Q FP8 needs FP8 rows
   if (qf) return launch_decode_hd<true, true>(p, stream);

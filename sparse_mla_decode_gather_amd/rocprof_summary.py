@@ -36,7 +36,7 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-DECODE = ("decode_kernel", "decode_hd_kernel")   # the decode kernels (not gather_only)
+DECODE = ("decode_h64_kernel", "decode_hd_kernel")   # the decode kernels (not gather_only)
 COPY_PATTERNS = ("copy", "Copy")
 
 
