@@ -207,26 +207,28 @@ def test_topk_edges_ragged_tiles_and_masks():
         check(custom(idx, lens=lens, H=H, sinks=False), what=f"edges H={H} nosink")
 
 
-def test_large_logit_range_restarts_are_exact():
+@pytest.mark.parametrize("H", [64, 128])
+def test_large_logit_range_restarts_are_exact(H):
     """Logits spread far wider than the 64 (base-2) slack the kernel allows
     above its first-tile reference max, so later tiles force the split to
-    restart with a higher reference; the result must still match."""
+    restart with a higher reference (at H=64 the two waves of a head block
+    then agree on the larger raised max); the result must still match."""
     need_gpu()
     rng = np.random.default_rng(11)
     idx = np.concatenate([rng.integers(0, 600, (4, 128)),
                           rng.integers(0, 900, (4, 1400))], 1).astype(np.int32)
     # scores ~ N(0, (2*sqrt(512))^2): std ~45 natural, ~65 in base 2
-    w = custom(idx, lens=[1528, 900, 200, 1528], b1=2.0)
-    check(w, what="wide logits unsplit", plan=L.plan_splits(4, 128, 1528, num_splits=1))
-    check(w, what="wide logits S=4", plan=L.plan_splits(4, 128, 1528, num_splits=4))
+    w = custom(idx, lens=[1528, 900, 200, 1528], H=H, b1=2.0)
+    check(w, what=f"wide logits H={H} unsplit", plan=L.plan_splits(4, H, 1528, num_splits=1))
+    check(w, what=f"wide logits H={H} S=4", plan=L.plan_splits(4, H, 1528, num_splits=4))
 
 
 @pytest.mark.parametrize("dt", [W.BF16, W.FP8])
 def test_increasing_logits_force_repeated_restarts(dt):
     """Row i of the table is (i/40)*u for a fixed direction u and q = u, so
-    the logits rise by ~37 (base-2) every 32-row tile and the 64 units of
-    slack are outgrown every other tile.  FP8 rows round i/40 to E4M3 (the
-    oracle reads the same bits)."""
+    the logits rise by ~37 (base-2) every 32 rows and the 64 units of slack
+    are outgrown every 64 rows (every tile of the H=64 kernel).  FP8 rows
+    round i/40 to E4M3 (the oracle reads the same bits)."""
     need_gpu()
     T, K, H = 2, 700, 64
     tdt = torch.float8_e4m3fn if dt == W.FP8 else torch.bfloat16
@@ -273,7 +275,8 @@ def test_fp8_rows_edges_segments_and_restarts(H, q):
     (one register set: each row of tile i+1 is stored and the same row of
     tile i+2 loaded inside the S^T MFMAs of tile i; the first tile, the last
     and the drain are separate compile-time iterations); at H=64 they are
-    loaded through registers one tile ahead; in both kernels FP8 rows (and
+    loaded through registers one 64-row tile ahead (during the S^T MFMAs of
+    a tile, stored during its O^T MFMAs); in both kernels FP8 rows (and
     FP8 q) are widened exactly to BF16 and multiplied on the BF16 MFMA.
     Ragged and tiny lengths give odd, single and empty tile counts; K=5000
     crosses segments; wide logits force restarts."""
