@@ -12,14 +12,15 @@
 //
 // Kernel design (ours, for CDNA4; the pages' TRTLLM-gen / CuTe kernels are
 // prior art only):
-//  * One workgroup of 4 wave64s per (token, split), one wave per SIMD.  All H heads of the token live in the workgroup, so each gathered
-//    row is read from HBM once per (token, split) and reused by every head.
+//  * One workgroup of 4 wave64s per (token, split), one wave per SIMD.  All H
+//    heads of the token live in the workgroup, so each gathered row is read
+//    from HBM once per (token, split) and reused by every head.
 //  * The split's table columns are compacted first (masked, -1, truncated
 //    and out-of-range slots are dropped), so tiles are dense.
 //  * Rows are gathered 32 at a time (64 in decode_h64_kernel) into
-//    row-major LDS tiles with a padded
-//    pitch (conflict-free row and transposed reads), by LDS-DMA for BF16
-//    rows and through registers for FP8 rows and packed block-scaled rows
+//    row-major LDS tiles with a padded pitch (conflict-free row and
+//    transposed reads), by LDS-DMA for BF16 rows and through registers for
+//    FP8 rows and packed block-scaled rows
 //    (widened to BF16 on the way; every E4M3FN value, and every E4M3FN value
 //    times a power of two in BF16's normal range, is exactly a BF16 value).
 //  * S^T = K Q^T on MFMA 32x32x16 BF16 (A = tile rows from LDS, B = 32
@@ -458,6 +459,67 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
   return 8 * (i >> 2) + 4 * kg + (i & 3);
 }
 
+// The work item (token, split) a workgroup of 256 threads runs, XCD-aware:
+// the hardware hands consecutive workgroup ids to the 8 XCDs round-robin,
+// so each XCD gets a contiguous range of work items; the splits of one token
+// and neighbouring tokens (which share rows in speculative decode) then run
+// together on one XCD and share its L2.  XCD x owns the item range
+// [lo, lo + cnt) and starts its workgroups in the order of blockIdx.x >> 3.
+// With per-token lengths, and more items than CUs (the host sets
+// rank_items; with one item per CU the order cannot matter and the ranking
+// would only put a dependent load in front of every item's own loads), the
+// items of the range are started longest first (rank by active columns of
+// the item's split, ties by position): with one or two items per CU, taking
+// them in token order lets the CUs that draw two long tokens set the end of
+// a ragged batch (~9% at 512 tokens of topk_len uniform in [1024, 2048]);
+// longest-first recovers it for ~0.5% on uniform batches.  Up to one item
+// per thread; `lens` (cnt entries) and `pick` are LDS scratch, and every
+// thread of the workgroup must call this.
+template <bool GEN>
+__device__ __forceinline__ int pick_item(const DecodeParams& p, int32_t* lens,
+                                         int32_t* pick) {
+  constexpr int NT = 256;
+  const int nblk = gridDim.x;
+  const int xcd = blockIdx.x & 7;
+  const int q8 = nblk >> 3, r8 = nblk & 7;
+  const int lo = xcd * q8 + min(xcd, r8);
+  int item = lo + (blockIdx.x >> 3);
+  const int cnt = q8 + (xcd < r8 ? 1 : 0);
+  const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
+                          : p.topk_lens != nullptr;
+  if (p.rank_items && ragged && cnt > 1 && cnt <= NT) {
+    const int tid = threadIdx.x;
+    int my_len = -1;
+    if (tid < cnt) {
+      // active columns of the item's split: [0, L1) and, for the general
+      // table view, [P, P + L2), intersected with the split's columns
+      const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
+      int a, b;
+      token_length_loads<GEN>(p, ti, a, b);
+      TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
+      token_lengths<GEN>(p, a, b, ti_tab);
+      const int c0 = si * p.split_cols, c1 = c0 + p.split_cols;
+      my_len = max(0, min(ti_tab.L1, c1) - c0);
+      if constexpr (GEN)
+        my_len += max(0, min(ti_tab.P + ti_tab.L2, c1) - max(ti_tab.P, c0));
+      lens[tid] = my_len;
+    }
+    __syncthreads();
+    if (tid < cnt) {
+      int rank = 0;
+      for (int k = 0; k < cnt; ++k) {
+        const int lk = lens[k];
+        rank += (lk > my_len || (lk == my_len && k < tid)) ? 1 : 0;
+      }
+      if (rank == (int)(blockIdx.x >> 3)) *pick = lo + tid;
+    }
+    __syncthreads();
+    item = *pick;
+    __syncthreads();   // the scratch is free again
+  }
+  return item;
+}
+
 // ---------------------------------------------------------------------------
 // split kernel, H = 128 with BF16 rows: heads for S, output dims for O
 // ---------------------------------------------------------------------------
@@ -522,60 +584,8 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   const int l32 = lane & 31;
   const int kg = lane >> 5;
 
-  // XCD-aware work mapping: the hardware hands consecutive workgroup ids to
-  // the 8 XCDs round-robin, so each XCD gets a contiguous range of work
-  // items; the splits of one token and neighbouring tokens (which share rows
-  // in speculative decode) then run together on one XCD and share its L2.
-  // XCD x owns the item range [lo, lo + cnt) and starts its workgroups in
-  // the order of blockIdx.x >> 3.  With per-token lengths, and more items than CUs (the
-  // host sets rank_items; with one item per CU the order cannot matter and
-  // the ranking would only put a dependent load in front of every item's
-  // own loads), the items of the range are started longest first (rank by active columns of the item's split, ties
-  // by position): with one or two items per CU, taking them in token order
-  // lets the CUs that draw two long tokens set the end of a ragged batch
-  // (~9% at 512 tokens of topk_len uniform in [1024, 2048]); longest-first
-  // recovers it for ~0.5% on uniform batches.  The ranking uses slots[],
-  // which the compaction fills only later.  Up to one item per thread.
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int q8 = nblk >> 3, r8 = nblk & 7;
-  const int lo = xcd * q8 + min(xcd, r8);
-  int item = lo + (blockIdx.x >> 3);
-  {
-    const int cnt = q8 + (xcd < r8 ? 1 : 0);
-    const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
-                            : p.topk_lens != nullptr;
-    if (p.rank_items && ragged && cnt > 1 && cnt <= NT) {
-      const int tid = threadIdx.x;
-      int my_len = -1;
-      if (tid < cnt) {
-        // active columns of the item's split: [0, L1) and, for the general
-        // table view, [P, P + L2), intersected with the split's columns
-        const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
-        int a, b;
-        token_length_loads<GEN>(p, ti, a, b);
-        TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
-        token_lengths<GEN>(p, a, b, ti_tab);
-        const int c0 = si * p.split_cols, c1 = c0 + p.split_cols;
-        my_len = max(0, min(ti_tab.L1, c1) - c0);
-        if constexpr (GEN)
-          my_len += max(0, min(ti_tab.P + ti_tab.L2, c1) - max(ti_tab.P, c0));
-        slots[tid] = my_len;
-      }
-      __syncthreads();
-      if (tid < cnt) {
-        int rank = 0;
-        for (int k = 0; k < cnt; ++k) {
-          const int lk = slots[k];
-          rank += (lk > my_len || (lk == my_len && k < tid)) ? 1 : 0;
-        }
-        if (rank == (int)(blockIdx.x >> 3)) slots[kSegHd] = lo + tid;
-      }
-      __syncthreads();
-      item = slots[kSegHd];
-      __syncthreads();   // slots[] is rewritten by the compaction
-    }
-  }
+  // the work item (see pick_item); slots[] is free until the compaction
+  const int item = pick_item<GEN>(p, slots, slots + kSegHd);
   const int t = item / p.S;
   const int s = item - t * p.S;
   const int head = wave * 32 + l32;       // head of this lane's S^T column
@@ -1209,12 +1219,13 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
 // rows, with P^T exchanged through LDS in the O^T MFMAs' B-operand layout
 // (as in decode_hd_kernel).  (Two workgroups of two waves, each wave
 // holding 32 heads of O for all 512 dims, would make every wave read the
-// whole tile for both products: a third more LDS reads per row.)  Two LDS stages of 64 rows: the rows of tile i+1 go out
-// during the S^T MFMAs of tile i, by LDS-DMA (BF16 rows) or into registers
-// (FP8 and packed rows; widened and written to their stage between the O^T
-// MFMAs of tile i, the stage tile i-1 used).  The two waves that share a
-// head block share its reference max: the first tile's is the max over both
-// row blocks (exchanged through LDS), and a restart takes the larger of the
+// whole tile for both products: a third more LDS reads per row.)
+// Two LDS stages of 64 rows: the rows of tile i+1 go out during the S^T
+// MFMAs of tile i, by LDS-DMA (BF16 rows) or into registers (FP8 and
+// packed rows; widened and written to their stage between the O^T MFMAs of
+// tile i, the stage tile i-1 used).  The two waves that share a head block
+// share its reference max: the first tile's is the max over both row
+// blocks (exchanged through LDS), and a restart takes the larger of the
 // two waves' raised maxima.  The normaliser adds the two waves' sums.
 template <bool Q_FP8, bool KV_FP8, bool SPLIT, bool GEN, bool PACKED = false,
           bool SERIAL = false>
@@ -1254,46 +1265,8 @@ void decode_h64_kernel(DecodeParams p) {
   const int hbs = wave & 1, rbs = wave >> 1;   // this wave's S^T block
   const int head = hbs * 32 + l32;             // head of this lane's S^T column
 
-  // XCD-aware work mapping, longest item first when a CU gets more than
-  // one (see decode_hd_kernel)
-  const int nblk = gridDim.x;
-  const int xcd = blockIdx.x & 7;
-  const int q8 = nblk >> 3, r8 = nblk & 7;
-  const int lo = xcd * q8 + min(xcd, r8);
-  int item = lo + (blockIdx.x >> 3);
-  {
-    const int cnt = q8 + (xcd < r8 ? 1 : 0);
-    const bool ragged = GEN ? (p.topk_lens != nullptr || p.lens2 != nullptr)
-                            : p.topk_lens != nullptr;
-    if (p.rank_items && ragged && cnt > 1 && cnt <= NT) {
-      const int tid = threadIdx.x;
-      int my_len = -1;
-      if (tid < cnt) {
-        const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
-        int a, b;
-        token_length_loads<GEN>(p, ti, a, b);
-        TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
-        token_lengths<GEN>(p, a, b, ti_tab);
-        const int c0 = si * p.split_cols, c1 = c0 + p.split_cols;
-        my_len = max(0, min(ti_tab.L1, c1) - c0);
-        if constexpr (GEN)
-          my_len += max(0, min(ti_tab.P + ti_tab.L2, c1) - max(ti_tab.P, c0));
-        slots[tid] = my_len;
-      }
-      __syncthreads();
-      if (tid < cnt) {
-        int rank = 0;
-        for (int k = 0; k < cnt; ++k) {
-          const int lk = slots[k];
-          rank += (lk > my_len || (lk == my_len && k < tid)) ? 1 : 0;
-        }
-        if (rank == (int)(blockIdx.x >> 3)) slots[kSegHd] = lo + tid;
-      }
-      __syncthreads();
-      item = slots[kSegHd];
-      __syncthreads();   // slots[] is rewritten by the compaction
-    }
-  }
+  // the work item (see pick_item); slots[] is free until the compaction
+  const int item = pick_item<GEN>(p, slots, slots + kSegHd);
   const int t = item / p.S;
   const int s = item - t * p.S;
 
@@ -1549,7 +1522,8 @@ void decode_h64_kernel(DecodeParams p) {
           if (more) {
 #pragma unroll
             for (int r = 0; r < PER; ++r)
-              lds_dma_row16<false, true>(rr[r], lane_off, dn + (uint32_t)((q * PER + r) * kRowPitch));
+              lds_dma_row16<false, true>(rr[r], lane_off,
+                                         dn + (uint32_t)((q * PER + r) * kRowPitch));
           }
           if (q + 1 < 8) {
 #pragma unroll
