@@ -337,7 +337,8 @@ def other_workloads(stream, only=None, settle_ms=SETTLE_MS):
         t_roof = max(gathered / (HBM_PEAK_GBPS * 1e9),
                      flops / (MFMA_PEAK_BY_ROWS[w.kv_dtype] * 1e12))
         res[name] = {"T": w.T, "H": w.H, "K": w.K, "q": w.q_dtype, "kv": w.kv_dtype,
-                     "num_splits": plan.num_splits, "gathered_bytes": gathered,
+                     "num_splits": plan.num_splits, "head_tiles": plan.head_tiles,
+                     "gathered_bytes": gathered,
                      "launch_us": round(avg * 1e3, 2),
                      "graph_launch_us": round(gms * 1e3, 2),
                      "gathered_GBps": round(gathered / (gms * 1e-3) / 1e9, 1),
@@ -594,7 +595,7 @@ def main():
             sweep[str(t)] = {"tokens_per_s": round(t * 50 / (tot * 1e-3), 1),
                              "avg_launch_us": round(avg * 1e3, 2),
                              "gathered_GBps": round(g / (avg * 1e-3) / 1e9, 1),
-                             "num_splits": p.num_splits,
+                             "num_splits": p.num_splits, "head_tiles": p.head_tiles,
                              "roofline_frac": round(g / (HBM_PEAK_GBPS * 1e9) /
                                                     (avg * 1e-3), 4)}
             if t <= 16:

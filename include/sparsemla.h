@@ -120,14 +120,18 @@ typedef struct ihipStream_t* smla_stream_t;
  * [s*chunks_per_split*chunk_cols, (s+1)*chunks_per_split*chunk_cols).  A
  * split whose columns are all inactive yields an empty partial.  A plan
  * passed to a decode call must have 1 <= num_splits <= SMLA_MAX_SPLITS,
- * chunk_cols and chunks_per_split >= 1, K equal to the call's K, and span
+ * chunk_cols and chunks_per_split >= 1, K equal to the call's K, span
  * num_splits * chunks_per_split * chunk_cols columns with
- * K <= span <= SMLA_MAX_PLAN_COLUMNS; otherwise the call returns
- * SMLA_ERR_BAD_PLAN. */
+ * K <= span <= SMLA_MAX_PLAN_COLUMNS, and head_tiles 1, or 2 at H=128;
+ * otherwise the call returns SMLA_ERR_BAD_PLAN. */
 #define SMLA_MAX_PLAN_COLUMNS (1 << 30)
 typedef struct smla_plan {
   int32_t num_splits;        /* S >= 1; S == 1 writes out/out_lse directly */
-  int32_t head_tiles;        /* always 1: one workgroup covers all heads */
+  int32_t head_tiles;        /* 1: one workgroup covers all heads; 2 (H=128
+                                only): each token runs as two 64-head
+                                halves, each gathering the token's rows
+                                (the second read mostly from L2); same
+                                workspace, same outputs up to rounding */
   int32_t chunk_cols;        /* columns per chunk */
   int32_t chunks_per_split;  /* consecutive chunks per split */
   int32_t num_chunks;        /* ceil(K / chunk_cols) */
@@ -189,8 +193,12 @@ typedef struct smla_decode_args {
  *   caches it per device.
  *   Every row format is widened and multiplied on the BF16 MFMA, so a
  *   split's time follows its row count, not its bytes.  The row format
- *   changes the plan only at H=64, where BF16 rows (gathered straight into
- *   LDS) cost half as much as rows staged through registers (FP8, packed).
+ *   changes the plan only through the H=64 kernel, where BF16 rows
+ *   (gathered straight into LDS) cost half as much as rows staged through
+ *   registers (FP8, packed).  At H=128 the planner also weighs head tiles
+ *   (head_tiles = 2, with its own split count) against one workgroup per
+ *   token and split: they pay at small and mid T, where the grid is short
+ *   of workgroups; an override of num_splits keeps head_tiles = 1.
  * Returns SMLA_ERR_INVALID_ARG for T < 0, K < 1, K > SMLA_MAX_PLAN_COLUMNS
  * or a NULL out_plan,
  * SMLA_ERR_UNSUPPORTED_SHAPE for H not in {64,128},
@@ -402,10 +410,12 @@ int sparse_mla_build_indices(const smla_build_args* args, smla_stream_t stream);
 /* Measurement aid (not part of the method): run only the table compaction
  * and the row gather of sparse_mla_decode on the same arguments and plan,
  * with no arithmetic and no output, to give the attainable gathered-row
- * bandwidth on these exact tables (a companion pure-gather benchmark).  Same argument checks as sparse_mla_decode except that out,
- * out_lse and the workspace are not used; only H = 128 with BF16 q and
- * rows is supported (else SMLA_ERR_UNSUPPORTED_SHAPE / _DTYPE).
- * Asynchronous on "stream"; no allocation. */
+ * bandwidth on these exact tables (a companion pure-gather benchmark).
+ * Same argument checks as sparse_mla_decode except that out, out_lse and
+ * the workspace are not used, and the plan's head_tiles is ignored (the
+ * gather has no heads; each token's rows are gathered once); only H = 128
+ * with BF16 q and rows is supported (else SMLA_ERR_UNSUPPORTED_SHAPE /
+ * _DTYPE).  Asynchronous on "stream"; no allocation. */
 int sparse_mla_gather_only(const smla_decode_args* args, const smla_plan* plan,
                            smla_stream_t stream);
 

@@ -29,6 +29,22 @@ constexpr int kChunkCols = 64;          // split granularity in table columns
 constexpr int64_t kWgOverheadRows = 96;
 constexpr int64_t kPartialPerHead = 1;
 constexpr int64_t kCombinePerRow = 4;
+constexpr int64_t kHeadTileNum = 5, kHeadTileDen = 4;
+
+// The model's cost of S = s splits for T tokens of H heads (one workgroup
+// per CU): rounds of workgroups times a workgroup's fixed cost, its rows
+// and its partial write, plus the combine's reads spread over the CUs.
+int64_t split_cost(int64_t T, int H, int K, int num_chunks, int s, int64_t row_w,
+                   int num_cus) {
+  const int64_t cps = (num_chunks + s - 1) / s;
+  const int64_t rows = std::min<int64_t>(cps * kChunkCols, K);
+  const int64_t waves = (T * s + num_cus - 1) / num_cus;
+  const int64_t per_wg = 2 * kWgOverheadRows + rows * row_w +
+                         (s > 1 ? kPartialPerHead * (int64_t)H : 0);
+  int64_t cost = waves * per_wg;
+  if (s > 1) cost += (kCombinePerRow * T * H * s + num_cus - 1) / num_cus;
+  return cost;
+}
 
 std::mutex g_cu_mutex;
 int g_cu_count[64] = {0};
@@ -90,6 +106,7 @@ constexpr int64_t kMaxPlanColumns = SMLA_MAX_PLAN_COLUMNS;
 
 bool plan_ok(const smla_plan* p, int K) {
   if (p->num_splits < 1 || p->num_splits > SMLA_MAX_SPLITS) return false;
+  if (p->head_tiles != 1 && p->head_tiles != 2) return false;
   if (p->chunk_cols < 1 || p->chunks_per_split < 1) return false;
   if (p->K != K) return false;
   const int64_t split_cols = (int64_t)p->chunks_per_split * p->chunk_cols;
@@ -124,44 +141,58 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
   int cap = max_splits > 0 ? max_splits : kDefaultMaxSplits;
   cap = std::min(std::min(cap, num_chunks), SMLA_MAX_SPLITS);
 
-  int S = 1;
+  int S = 1, head_tiles = 1;
   if (num_splits_override > 0) {
     S = std::min(std::max(num_splits_override, 1),
                  std::min(num_chunks, SMLA_MAX_SPLITS));
   } else if (T > 0) {
-    // Workgroups resident per CU: one (at H=128 each wave holds 32 heads of
-    // O in registers; at H=64 the 64-row tiles of the four-wave kernel fill
-    // the LDS).
-    const int64_t slots = num_cus;
-    // Per-row cost: the same for every row format.  Rows are widened to BF16
-    // and multiplied on the BF16 MFMA, whose work per row is the same, so
-    // the row count and not its bytes sets a split's time (weighting FP8
-    // rows by their half-size bytes picked one split where 4-8 ran up to
-    // 1.5x faster: H=128 FP8 rows, K=512, T=16-48).  At H=64 a BF16 row,
-    // gathered by LDS-DMA, costs half of one staged through registers (FP8
-    // and packed rows), which at H=128 the MFMA work hides (fitted on
-    // sweeps of forced splits at H=64, BF16 and FP8 rows, K = 512 .. 2048,
-    // T = 1 .. 512).
-    const int64_t row_w = (H == 64 && kv_dtype == SMLA_DTYPE_BF16) ? 1 : 2;
+    // Per-row cost: the same for every row format at H=128.  Rows are
+    // widened to BF16 and multiplied on the BF16 MFMA, whose work per row is
+    // the same, so the row count and not its bytes sets a split's time
+    // (weighting FP8 rows by their half-size bytes picked one split where
+    // 4-8 ran up to 1.5x faster: H=128 FP8 rows, K=512, T=16-48).  At H=64
+    // a BF16 row, gathered by LDS-DMA, costs half of one staged through
+    // registers (FP8 and packed rows), which at H=128 the MFMA work hides
+    // (fitted on sweeps of forced splits at H=64, BF16 and FP8 rows,
+    // K = 512 .. 2048, T = 1 .. 512).
+    const int64_t row_w64 = kv_dtype == SMLA_DTYPE_BF16 ? 1 : 2;
+    const int64_t row_w = H == 64 ? row_w64 : 2;
+    // An H=128 call may also run as head tiles: each token as two 64-head
+    // halves on the H=64 kernel (2T virtual tokens, rows read twice, the
+    // second time mostly from L2).  Their cost is the H=64 model's with a
+    // row weight of 1 for BF16 and FP8 rows alike (against the H=128
+    // kernel, which stages FP8 rows through registers too), and one unit of
+    // it is worth kHeadTileNum / kHeadTileDen units of the H=128 model
+    // (fitted on forced plans of both forms: BF16 rows, K = 512 .. 2048,
+    // T = 1 .. 192; FP8 rows, K = 512 and 2048, T = 4 .. 128; mean loss
+    // against the fastest 0.6%, worst 7.6%).  Packed rows keep one
+    // workgroup per token: head tiles were not measured with them.
+    const bool try_head_tiles = H == 128 && kv_dtype != SMLA_DTYPE_PACKED_FP8_584;
+    const int64_t w_own = try_head_tiles ? kHeadTileDen : 1;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {
-      const int64_t cps = (num_chunks + s - 1) / s;
-      const int64_t rows = std::min<int64_t>(cps * kChunkCols, K);
-      const int64_t waves = ((int64_t)T * s + slots - 1) / slots;
-      const int64_t per_wg = 2 * kWgOverheadRows + rows * row_w +
-                             (s > 1 ? kPartialPerHead * (int64_t)H : 0);
-      int64_t cost = waves * per_wg;
-      if (s > 1)
-        cost += (kCombinePerRow * (int64_t)T * H * s + num_cus - 1) / num_cus;
+      const int64_t cost =
+          w_own * split_cost(T, H, K, num_chunks, s, row_w, num_cus);
       if (cost < best) {
         best = cost;
         S = s;
       }
     }
+    if (try_head_tiles) {
+      for (int s = 1; s <= cap; ++s) {
+        const int64_t cost =
+            kHeadTileNum * split_cost(2 * (int64_t)T, 64, K, num_chunks, s, 1, num_cus);
+        if (cost < best) {
+          best = cost;
+          S = s;
+          head_tiles = 2;
+        }
+      }
+    }
   }
   const int cps = (num_chunks + S - 1) / S;
   out_plan->num_splits = S;
-  out_plan->head_tiles = 1;
+  out_plan->head_tiles = head_tiles;
   out_plan->chunk_cols = kChunkCols;
   out_plan->chunks_per_split = cps;
   out_plan->num_chunks = num_chunks;
@@ -286,7 +317,10 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   }
   if (!plan_ok(plan, a->K)) return SMLA_ERR_BAD_PLAN;
   const int S = plan->num_splits;
-  if ((int64_t)a->T * S > INT_MAX) return SMLA_ERR_INVALID_ARG;
+  if ((int64_t)a->T * S > INT_MAX / 2) return SMLA_ERR_INVALID_ARG;
+  // head tiles: H=128 only; the gather alone has no heads and ignores them
+  if (plan->head_tiles == 2 && a->H != 128) return SMLA_ERR_BAD_PLAN;
+  const bool head_tiles = with_outputs && plan->head_tiles == 2;
 
   const bool validate = with_outputs && (a->flags & SMLA_FLAG_VALIDATE_INDICES) != 0;
   *L = layout_for(with_outputs ? S : 1, a->T, a->H, validate ? a->flags : 0);
@@ -323,8 +357,10 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   p->out = a->out;
   p->out_lse = a->out_lse;
   p->err = validate ? reinterpret_cast<int32_t*>(ws) : nullptr;
-  p->T = a->T;
-  p->H = a->H;
+  // head tiles: the H=64 kernel on 2T virtual tokens (same buffers)
+  p->T = head_tiles ? 2 * a->T : a->T;
+  p->H = head_tiles ? 64 : a->H;
+  p->head_shift = head_tiles ? 1 : 0;
   p->K = a->K;
   p->S = S;
   p->split_cols = plan->chunks_per_split * plan->chunk_cols;
@@ -333,7 +369,7 @@ int prepare_call(const smla_decode_args* a, const smla_segments* seg,
   // H=128 workgroup fits a CU); without a device count, keep them.
   {
     int cus = 0;
-    p->rank_items = (query_cu_count(&cus) != SMLA_OK || (int64_t)a->T * S > cus) ? 1 : 0;
+    p->rank_items = (query_cu_count(&cus) != SMLA_OK || (int64_t)p->T * S > cus) ? 1 : 0;
   }
   p->serial = serial ? 1 : 0;
   if (with_outputs && S > 1) {

@@ -61,6 +61,11 @@ struct DecodeParams {
   // launch the serialized tile pipeline (SMLA_FLAG_SERIAL_PIPELINE: an
   // LDS-race check, combined table only); read by the host dispatch
   int32_t serial;
+  // head tiles: 0, or 1 when each token runs as two 64-head halves (the
+  // H=64 kernel on 2T virtual tokens: virtual token v is token v >> 1,
+  // heads 64 (v & 1) ..; q, out and the partials keep their [T, 128, ...]
+  // layout, which is [2T, 64, ...])
+  int32_t head_shift;
 };
 
 struct CombineParams {

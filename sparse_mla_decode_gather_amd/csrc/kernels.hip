@@ -474,10 +474,11 @@ __device__ __forceinline__ int tile_row_of_reg(int i, int kg) {
 // a ragged batch (~9% at 512 tokens of topk_len uniform in [1024, 2048]);
 // longest-first recovers it for ~0.5% on uniform batches.  Up to one item
 // per thread; `lens` (cnt entries) and `pick` are LDS scratch, and every
-// thread of the workgroup must call this.
+// thread of the workgroup must call this.  head_shift: items count virtual
+// tokens, token v >> head_shift of the table (head tiles).
 template <bool GEN>
 __device__ __forceinline__ int pick_item(const DecodeParams& p, int32_t* lens,
-                                         int32_t* pick) {
+                                         int32_t* pick, int head_shift) {
   constexpr int NT = 256;
   const int nblk = gridDim.x;
   const int xcd = blockIdx.x & 7;
@@ -493,7 +494,8 @@ __device__ __forceinline__ int pick_item(const DecodeParams& p, int32_t* lens,
     if (tid < cnt) {
       // active columns of the item's split: [0, L1) and, for the general
       // table view, [P, P + L2), intersected with the split's columns
-      const int ti = (lo + tid) / p.S, si = lo + tid - ti * p.S;
+      const int vi = (lo + tid) / p.S, si = lo + tid - vi * p.S;
+      const int ti = vi >> head_shift;
       int a, b;
       token_length_loads<GEN>(p, ti, a, b);
       TokenTable<GEN, false> ti_tab = token_table<GEN, false>(p, ti);
@@ -585,7 +587,7 @@ __device__ __forceinline__ void decode_hd_body(const DecodeParams& p) {
   const int kg = lane >> 5;
 
   // the work item (see pick_item); slots[] is free until the compaction
-  const int item = pick_item<GEN>(p, slots, slots + kSegHd);
+  const int item = pick_item<GEN>(p, slots, slots + kSegHd, 0);
   const int t = item / p.S;
   const int s = item - t * p.S;
   const int head = wave * 32 + l32;       // head of this lane's S^T column
@@ -1265,10 +1267,15 @@ void decode_h64_kernel(DecodeParams p) {
   const int hbs = wave & 1, rbs = wave >> 1;   // this wave's S^T block
   const int head = hbs * 32 + l32;             // head of this lane's S^T column
 
-  // the work item (see pick_item); slots[] is free until the compaction
-  const int item = pick_item<GEN>(p, slots, slots + kSegHd);
-  const int t = item / p.S;
-  const int s = item - t * p.S;
+  // the work item (see pick_item); slots[] is free until the compaction.
+  // With head tiles (an H=128 call) item v of the grid is virtual token
+  // vt: table token t = vt >> 1, heads hoff + 0..63; q, the output and the
+  // partials are indexed by vt, in the H=128 layout seen as 64 heads.
+  const int item = pick_item<GEN>(p, slots, slots + kSegHd, p.head_shift);
+  const int vt = item / p.S;
+  const int s = item - vt * p.S;
+  const int t = vt >> p.head_shift;
+  const int hoff = (vt & ((1 << p.head_shift) - 1)) * H;
 
   // table entries, then Q (see decode_hd_kernel)
   const int c_begin = s * p.split_cols;
@@ -1286,7 +1293,7 @@ void decode_h64_kernel(DecodeParams p) {
   __builtin_amdgcn_sched_barrier(0);
   bf16x8 qf[32];
   {
-    const size_t qrow = ((size_t)t * H + head) * kD;
+    const size_t qrow = ((size_t)vt * H + head) * kD;
 #pragma unroll
     for (int kk = 0; kk < 32; ++kk) {
       const int d0 = kk * 16 + kg * 8;
@@ -1658,7 +1665,7 @@ void decode_h64_kernel(DecodeParams p) {
     } else {
       float fac = 1.f;
       if (p.sinks) {
-        const float sl = p.sinks[head] * kLog2e;
+        const float sl = p.sinks[hoff + head] * kLog2e;
         const float mm = fmaxf(m, sl);
         fac = fast_exp2(m - mm);        // 0 when nothing was active (m = -inf)
         l = l * fac + fast_exp2(sl - mm);
@@ -1669,8 +1676,8 @@ void decode_h64_kernel(DecodeParams p) {
     }
     if (kg == 0) {
       inv_lds[head] = inv;
-      if constexpr (SPLIT) p.mid_lse[((size_t)t * H + head) * p.S + s] = lse;
-      else if (p.out_lse) p.out_lse[(size_t)t * H + head] = lse;
+      if constexpr (SPLIT) p.mid_lse[((size_t)vt * H + head) * p.S + s] = lse;
+      else if (p.out_lse) p.out_lse[(size_t)vt * H + head] = lse;
     }
   }
   __syncthreads();
@@ -1701,9 +1708,9 @@ void decode_h64_kernel(DecodeParams p) {
     const u32x4 v = *(const u32x4*)(kv_lds + hh * kOutPitch + lane * 16);
     uint16_t* dst;
     if constexpr (SPLIT)
-      dst = p.mid_out + (((size_t)t * H + hh) * p.S + s) * kD;
+      dst = p.mid_out + (((size_t)vt * H + hh) * p.S + s) * kD;
     else
-      dst = (uint16_t*)p.out + ((size_t)t * H + hh) * kD;
+      dst = (uint16_t*)p.out + ((size_t)vt * H + hh) * kD;
     *(u32x4*)(dst + lane * 8) = v;
   }
 }

@@ -66,7 +66,7 @@ def plan(T, H=128, K=2048, q=0, kv=0, max_splits=0, override=0, cus=256):
 def test_plan_bounds(T, H, K):
     p = plan(T, H, K)
     assert 1 <= p.num_splits <= 16 and p.num_splits <= p.num_chunks
-    assert p.head_tiles == 1 and p.K == K
+    assert p.head_tiles in ((1, 2) if H == 128 else (1,)) and p.K == K
     assert p.num_chunks == -(-K // p.chunk_cols)
     assert p.num_splits * p.chunks_per_split * p.chunk_cols >= K
     # no split is entirely past the table
@@ -78,7 +78,7 @@ def test_plan_bounds(T, H, K):
 def test_plan_adapts_to_batch():
     # one chunk per block at low batch, a single chunk at high batch
     assert plan(1).num_splits == 16
-    assert plan(8).num_splits == 16
+    assert plan(8).num_splits >= 11      # 11 with head tiles (16 workgroups per half)
     assert plan(512).num_splits == 1
     assert plan(4096).num_splits == 1
     assert plan(1, max_splits=4).num_splits == 4
@@ -287,6 +287,8 @@ def test_decode_workspace_checks(so):
                setattr(p, "chunks_per_split", 1)),
     lambda p: (setattr(p, "num_splits", 1), setattr(p, "chunk_cols", 2),
                setattr(p, "chunks_per_split", (1 << 29) + 1)),
+    lambda p: setattr(p, "head_tiles", 0),
+    lambda p: setattr(p, "head_tiles", 3),
 ])
 def test_decode_rejects_bad_plan(so, mutate):
     a = good_args(T=4, K=2048)
@@ -632,35 +634,52 @@ def test_flags_unknown_bits_and_serial_pipeline_forms(so):
     assert call_gather(so, ga) == 1
 
 
-@pytest.mark.parametrize("T,H,K,kv,S", [
-    (4, 64, 256, 0, 4),        # tiny
-    (64, 128, 512, 0, 2),      # batched with sinks
-    (128, 64, 1024, 1, 2),     # FP8 q and rows
-    (1, 128, 2048, 0, 16), (4, 128, 2048, 0, 16), (8, 128, 2048, 0, 16),
-    (16, 128, 2048, 0, 11), (32, 128, 2048, 0, 8), (64, 128, 2048, 0, 4),
-    (128, 128, 2048, 0, 2), (512, 128, 2048, 0, 1),
-    (512, 128, 2048, 1, 1),    # speculative decode (FP8 rows, BF16 q)
-    (16, 128, 512, 1, 4),      # FP8 rows plan by row count, not bytes (was 1)
+@pytest.mark.parametrize("T,H,K,kv,S,HT", [
+    (4, 64, 256, 0, 4, 1),        # tiny
+    (64, 128, 512, 0, 1, 2),      # batched with sinks: head tiles, no split
+    (128, 64, 1024, 1, 2, 1),     # FP8 q and rows
+    (1, 128, 2048, 0, 16, 2), (4, 128, 2048, 0, 16, 2), (8, 128, 2048, 0, 11, 2),
+    (16, 128, 2048, 0, 8, 2), (32, 128, 2048, 0, 4, 2), (64, 128, 2048, 0, 4, 1),
+    (96, 128, 2048, 0, 2, 1), (128, 128, 2048, 0, 1, 2), (512, 128, 2048, 0, 1, 1),
+    (512, 128, 2048, 1, 1, 1),    # speculative decode (FP8 rows, BF16 q)
+    (16, 128, 512, 1, 4, 2),      # FP8 rows plan by row count, not bytes
+    (64, 128, 2048, 1, 4, 1), (16, 128, 2048, 1, 8, 2),
     # H=64, BF16 q and rows: one four-wave workgroup per CU
-    (16, 64, 2048, 0, 11), (64, 64, 512, 0, 2), (128, 64, 1024, 0, 2),
-    (512, 64, 2048, 0, 1),
+    (16, 64, 2048, 0, 11, 1), (64, 64, 512, 0, 2, 1), (128, 64, 1024, 0, 2, 1),
+    (512, 64, 2048, 0, 1, 1),
 ])
-def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S):
+def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S, HT):
     """The planner's picks for the benchmarked shapes on a 256-CU device
-    (each the fastest or within ~2% of the fastest forced split measured on
+    (each the fastest or within ~2% of the fastest forced plan measured on
     MI355X; the cost model is deterministic, so these are exact)."""
     q = 1 if (kv == 1 and H == 64) else 0
-    assert plan(T, H, K, q=q, kv=kv, cus=256).num_splits == S
+    p = plan(T, H, K, q=q, kv=kv, cus=256)
+    assert (p.num_splits, p.head_tiles) == (S, HT)
+
+
+def test_plan_head_tiles_only_at_h128_and_not_when_forced():
+    """Head tiles are an H=128 choice of the planner; a forced split count
+    keeps one workgroup per token and split."""
+    for T in (1, 4, 16, 64, 128):
+        assert plan(T, 64, 2048, cus=256).head_tiles == 1
+        assert plan(T, 128, 2048, override=4, cus=256).head_tiles == 1
+    assert plan(64, 128, 512, cus=256).head_tiles == 2
 
 
 def test_plan_h64_depends_on_the_row_format():
     """At H=64 a BF16 row (LDS-DMA) costs half a row staged through
     registers (FP8, packed), so the same shape can get fewer splits; at
-    H=128 the format never changes the plan."""
+    H=128 the format changes the plan only through head tiles, which
+    packed rows do not use."""
     assert plan(64, 64, 512, q=0, kv=0, cus=256).num_splits == 2
     assert plan(64, 64, 512, q=0, kv=1, cus=256).num_splits == 4
     assert plan(64, 64, 512, q=1, kv=1, cus=256).num_splits == 4
     assert plan(64, 64, 512, q=0, kv=2, cus=256).num_splits == 4
+    for kv in (0, 1):          # head tiles for BF16 and FP8 rows alike
+        p = plan(128, 128, 1024, q=0, kv=kv, cus=256)
+        assert (p.num_splits, p.head_tiles) == (1, 2)
+    p = plan(128, 128, 1024, q=0, kv=2, cus=256)   # packed rows: never
+    assert (p.num_splits, p.head_tiles) == (2, 1)
     for kv in (0, 1, 2):
-        assert plan(128, 128, 1024, q=0, kv=kv, cus=256).num_splits == \
-            plan(128, 128, 1024, q=0, kv=0, cus=256).num_splits
+        p = plan(512, 128, 2048, q=0, kv=kv, cus=256)
+        assert (p.num_splits, p.head_tiles) == (1, 1)
