@@ -193,9 +193,8 @@ typedef struct smla_decode_args {
  *   caches it per device.
  *   Every row format is widened and multiplied on the BF16 MFMA, so a
  *   split's time follows its row count, not its bytes.  The row format
- *   changes the plan only through the H=64 kernel, where BF16 rows
- *   (gathered straight into LDS) cost half as much as rows staged through
- *   registers (FP8, packed).  At H=128 the planner also weighs head tiles
+ *   changes the plan only at H=64, where BF16 rows (gathered straight into
+ *   LDS) cost half as much as rows staged through registers (FP8, packed).  At H=128 the planner also weighs head tiles
  *   (head_tiles = 2, with its own split count) against one workgroup per
  *   token and split: they pay at small and mid T, where the grid is short
  *   of workgroups; an override of num_splits keeps head_tiles = 1.

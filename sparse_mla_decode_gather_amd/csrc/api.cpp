@@ -161,13 +161,13 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     // halves on the H=64 kernel (2T virtual tokens, rows read twice, the
     // second time mostly from L2).  Their cost is the H=64 model's with a
     // row weight of 1 for BF16 and FP8 rows alike (against the H=128
-    // kernel, which stages FP8 rows through registers too), and one unit of
-    // it is worth kHeadTileNum / kHeadTileDen units of the H=128 model
-    // (fitted on forced plans of both forms: BF16 rows, K = 512 .. 2048,
-    // T = 1 .. 192; FP8 rows, K = 512 and 2048, T = 4 .. 128; mean loss
-    // against the fastest 0.6%, worst 7.6%).  Packed rows keep one
-    // workgroup per token: head tiles were not measured with them.
-    const bool try_head_tiles = H == 128 && kv_dtype != SMLA_DTYPE_PACKED_FP8_584;
+    // kernel, which stages FP8 and packed rows through registers too), and
+    // one unit of it is worth kHeadTileNum / kHeadTileDen units of the
+    // H=128 model (fitted on forced plans of both forms: BF16 rows,
+    // K = 512 .. 2048, T = 1 .. 192, FP8 rows, K = 512 and 2048, T = 4 .. 128,
+    // mean loss against the fastest 0.6%, worst 7.6%; packed rows, K = 512
+    // and 2048, T = 1 .. 128: mean 1.5%, worst 10.6%).
+    const bool try_head_tiles = H == 128;
     const int64_t w_own = try_head_tiles ? kHeadTileDen : 1;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {

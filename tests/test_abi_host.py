@@ -669,17 +669,15 @@ def test_plan_head_tiles_only_at_h128_and_not_when_forced():
 def test_plan_h64_depends_on_the_row_format():
     """At H=64 a BF16 row (LDS-DMA) costs half a row staged through
     registers (FP8, packed), so the same shape can get fewer splits; at
-    H=128 the format changes the plan only through head tiles, which
-    packed rows do not use."""
+    H=128 the format does not change the plan (head tiles weigh every
+    row format alike)."""
     assert plan(64, 64, 512, q=0, kv=0, cus=256).num_splits == 2
     assert plan(64, 64, 512, q=0, kv=1, cus=256).num_splits == 4
     assert plan(64, 64, 512, q=1, kv=1, cus=256).num_splits == 4
     assert plan(64, 64, 512, q=0, kv=2, cus=256).num_splits == 4
-    for kv in (0, 1):          # head tiles for BF16 and FP8 rows alike
+    for kv in (0, 1, 2):       # head tiles for every row format alike
         p = plan(128, 128, 1024, q=0, kv=kv, cus=256)
         assert (p.num_splits, p.head_tiles) == (1, 2)
-    p = plan(128, 128, 1024, q=0, kv=2, cus=256)   # packed rows: never
-    assert (p.num_splits, p.head_tiles) == (2, 1)
     for kv in (0, 1, 2):
         p = plan(512, 128, 2048, q=0, kv=kv, cus=256)
         assert (p.num_splits, p.head_tiles) == (1, 1)
