@@ -36,7 +36,8 @@
 //    quarter of the output dims of all heads, with P exchanged through LDS
 //    (see there).  decode_h64_kernel (H=64): the same split of O over four
 //    waves, with S of a 64-row tile split over the waves by head block and
-//    row block.  FP8 q and FP8 rows are widened exactly to BF16 and
+//    row block.  Head tiles (a plan choice at H=128) run an H=128 call on
+//    decode_h64_kernel as 2T virtual tokens of 64 heads each.  FP8 q and FP8 rows are widened exactly to BF16 and
 //    multiplied on the BF16 MFMA.
 //  * Unsplit: the epilogue adds the sink and writes out / out_lse.  Split:
 //    each split writes a BF16 partial and its base-2 LSE; a combine kernel
