@@ -160,8 +160,8 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     // An H=128 call may also run as head tiles: each token as two 64-head
     // halves on the H=64 kernel (2T virtual tokens, rows read twice, the
     // second time mostly from L2).  Their cost is the H=64 model's with a
-    // row weight of 1 for BF16 and FP8 rows alike (against the H=128
-    // kernel, which stages FP8 and packed rows through registers too), and
+    // row weight of 1 for every row format (against the H=128 kernel,
+    // which stages FP8 and packed rows through registers too), and
     // one unit of it is worth kHeadTileNum / kHeadTileDen units of the
     // H=128 model (fitted on forced plans of both forms: BF16 rows,
     // K = 512 .. 2048, T = 1 .. 192, FP8 rows, K = 512 and 2048, T = 4 .. 128,
