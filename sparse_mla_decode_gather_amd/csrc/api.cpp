@@ -166,8 +166,11 @@ int sparse_mla_plan_splits(int T, int H, int K, int q_dtype, int kv_dtype,
     // H=128 model (fitted on forced plans of both forms: BF16 rows,
     // K = 512 .. 2048, T = 1 .. 192, FP8 rows, K = 512 and 2048, T = 4 .. 128,
     // mean loss against the fastest 0.6%, worst 7.6%; packed rows, K = 512
-    // and 2048, T = 1 .. 128: mean 1.5%, worst 10.6%).
-    const bool try_head_tiles = H == 128;
+    // and 2048, T = 1 .. 128: mean 1.5%, worst 10.6%).  Only while 2T
+    // virtual tokens fit one round of CUs: beyond, the second row read and
+    // the extra rounds lose (T=384, K=2048: BF16 rows 2% and FP8 rows 15%
+    // slower than one workgroup per token, which the model misses).
+    const bool try_head_tiles = H == 128 && 2 * (int64_t)T <= num_cus;
     const int64_t w_own = try_head_tiles ? kHeadTileDen : 1;
     int64_t best = INT64_MAX;
     for (int s = 1; s <= cap; ++s) {

@@ -657,6 +657,16 @@ def test_plan_picks_on_a_256_cu_device(T, H, K, kv, S, HT):
     assert (p.num_splits, p.head_tiles) == (S, HT)
 
 
+@pytest.mark.parametrize("kv", [0, 1, 2])
+def test_plan_large_batches_keep_one_workgroup_per_token(kv):
+    """From T=192 on (measured: head tiles lose there, their second row read
+    and twice the workgroups outweigh the shorter MFMA chains) every format
+    and width keeps head_tiles = 1 at H=128."""
+    for K in (512, 1024, 2048, 4096):
+        for T in (192, 256, 384, 512, 1024, 4096):
+            assert plan(T, 128, K, q=0, kv=kv, cus=256).head_tiles == 1, (T, K)
+
+
 def test_plan_head_tiles_only_at_h128_and_not_when_forced():
     """Head tiles are an H=128 choice of the planner; a forced split count
     keeps one workgroup per token and split."""
